@@ -1,0 +1,265 @@
+"""Benchmark of the W4A16 linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode|mid|prefill|actorder|tiny]
+
+A step is one forward pass of the hot path over every (shape, M) case of the
+chosen workload: for each case one w4a16_linear call (host validation, kernel
+selection, fused dequantize + GEMM, epilogue) on activations and weights that
+are already resident in HBM.  The one-time repacks (AWQ -> standard ->
+tile layout) are timed separately and reported under "repack".
+
+Weight buffers are rotated over enough copies that every launch reads its
+weights from HBM (the working set exceeds the 256 MB Infinity Cache).
+
+Prints ONE JSON line.  ``value`` is packed-weight GB/s of the whole step
+(sum of K*N/2 over the cases / step time); ``roofline`` is for the GEMM
+kernel with achieved = algorithmic bytes per launch / HIP-event launch time;
+``cpu_baseline`` times the CPU oracle on a bounded sample of the workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 GEMM TFLOPS + packed-weight HBM GB/s (% roofline), M=1..8192"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+ROTATE_BYTES = 512 << 20       # working set per shape, > 256 MB MALL
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="decode", choices=["tiny", "decode", "mid", "prefill", "actorder"])
+    p.add_argument("--reps", type=int, default=0, help="launches per case for the per-kernel timing (0 = auto)")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    return p.parse_args()
+
+
+def _to_dev(torch, a):
+    """numpy -> cuda tensor; uint16 arrays are bf16 bit patterns."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def case_bytes(c, M):
+    """Algorithmic HBM bytes of one launch: packed weights + scales + zeros +
+    x + y (+ perm)."""
+    w = c.K * c.N // 2
+    s = c.G * c.N * 2
+    z = c.G * c.N // 2 if c.has_zeros else 0
+    x = M * c.K * 2
+    y = M * c.N * 2
+    p = c.K * 4 if c.has_gidx else 0
+    return w, w + s + z + x + y + p
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import weight_only_int4_gptq_amd as W
+    from synthetic import CONFIGS, make_acts, make_layer_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    W.lib()
+    cfg_id = {"tiny": 1, "decode": 2, "mid": 3, "prefill": 4, "actorder": 5}[args.config]
+    cases = [c for c in CONFIGS if c.cfg_id == cfg_id]
+    stream = torch.cuda.current_stream()
+
+    # ---- one-time repack (timed separately) and rotated weight copies ----
+    layers = []
+    repack = []
+    for c in cases:
+        Lw = make_layer_inputs(c)
+        dev = {k: _to_dev(torch, v) for k, v in Lw.items()}
+        lyr = W.W4A16Linear(c.K, c.N, c.group_size, c.has_zeros, c.has_gidx, c.dtype, c.fmt)
+        lyr.process_weights_after_loading(dev["qweight"], dev["qzeros"], dev["scales"], dev["g_idx"])  # warm
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lyr.process_weights_after_loading(dev["qweight"], dev["qzeros"], dev["scales"], dev["g_idx"])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rp_ms = e0.elapsed_time(e1)
+        repack.append({"shape": [c.K, c.N], "ms": round(rp_ms, 4),
+                       "packed_GBps": round((c.K * c.N / 2) / (rp_ms * 1e-3) / 1e9, 1)})
+        t = lyr.tiled
+        per_set = sum(v.numel() * v.element_size() for v in t.values() if v is not None)
+        R = max(2, math.ceil(ROTATE_BYTES / per_set))
+        sets = [t] + [{k: (v.clone() if v is not None else None) for k, v in t.items()} for _ in range(R - 1)]
+        del dev
+        layers.append((c, lyr, sets))
+    torch.cuda.synchronize()
+
+    # ---- activations / outputs per case ----
+    runs = []
+    for c, lyr, sets in layers:
+        for M in c.Ms:
+            x = make_acts(c, M)
+            xd = _to_dev(torch, x)
+            yd = torch.empty((M, c.N), dtype=xd.dtype, device="cuda")
+            ws_b = W.w4_workspace_size(lyr.layer, M)
+            ws = torch.zeros((max(ws_b, 1),), dtype=torch.uint8, device="cuda")
+            runs.append(dict(c=c, M=M, lyr=lyr, sets=sets, x=xd, y=yd, ws=ws, ws_b=ws_b, i=0,
+                             kernel=lyr.kernel_name(M)))
+
+    def launch(r):
+        t = r["sets"][r["i"] % len(r["sets"])]
+        r["i"] += 1
+        W.w4a16_linear(r["lyr"].layer, r["M"], r["x"], t["qweight"], t["scales"], t["qzeros"], t["perm"], None,
+                       r["y"], r["ws"] if r["ws_b"] else None, r["ws_b"], stream)
+
+    def step():
+        for r in runs:
+            launch(r)
+
+    # ---- per-kernel timing: HIP events on the launch stream ----
+    per_case = []
+    for r in runs:
+        c, M = r["c"], r["M"]
+        reps = args.reps or max(len(r["sets"]), 40)
+        for _ in range(5):
+            launch(r)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch(r)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        wb, tb = case_bytes(c, M)
+        flops = 2.0 * M * c.K * c.N
+        per_case.append(dict(K=c.K, N=c.N, M=M, kernel=r["kernel"], us=round(us, 3),
+                             weight_GBps=round(wb / (us * 1e-6) / 1e9, 1),
+                             total_GBps=round(tb / (us * 1e-6) / 1e9, 1),
+                             TFLOPS=round(flops / (us * 1e-6) / 1e12, 2),
+                             pct_hbm=round(100 * tb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+                             pct_mfma=round(100 * flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 1),
+                             _wb=wb, _tb=tb, _flops=flops, _us=us))
+
+    # ---- the timed steps ----
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    wbytes_step = sum(case_bytes(r["c"], r["M"])[0] for r in runs)
+    flops_step = sum(2.0 * r["M"] * r["c"].K * r["c"].N for r in runs)
+    value = wbytes_step / (ms_step * 1e-3) / 1e9
+
+    # roofline of the GEMM kernel: algorithmic bytes (or flops) / launch time
+    sum_tb = sum(p["_tb"] for p in per_case)
+    sum_fl = sum(p["_flops"] for p in per_case)
+    sum_us = sum(p["_us"] for p in per_case)
+    hbm_bound = (sum_fl / (sum_tb)) < (MFMA_F16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
+    if hbm_bound:
+        ach = sum_tb / (sum_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        ach = sum_fl / (sum_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = sorted({p["kernel"] for p in per_case})
+    roof["per_launch_bytes_avg"] = round(sum_tb / len(per_case))
+    roof["avg_launch_us"] = round(sum_us / len(per_case), 3)
+
+    cpu = None if args.no_cpu else cpu_baseline(cases, args.cpu_seconds)
+
+    for p in per_case:
+        for k in ("_wb", "_tb", "_flops", "_us"):
+            p.pop(k)
+    c0 = cases[0]
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if c0.dtype == "fp16" else "bf16",
+        "data": "synthetic (seeded uniform int4 codes/zeros, uniform scales, N(0,1) activations)",
+        "config": {
+            "workload": f"{args.config}: " + ", ".join(f"(K={c.K},N={c.N})" for c in cases)
+                        + f" x M in {list(c0.Ms)}; {c0.fmt.upper()} g={c0.group_size}"
+                        + (" zeros" if c0.has_zeros else " symmetric") + (" act-order" if c0.has_gidx else ""),
+            "cases": len(runs), "act_dtype": c0.dtype, "weight_rotation_MiB": ROTATE_BYTES >> 20,
+        },
+        "tflops_step": round(flops_step / (ms_step * 1e-3) / 1e12, 3),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_case": per_case,
+        "repack": repack,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cases, seconds):
+    """The CPU oracle, as it stands, on a bounded sample of the workload:
+    whole-layer reference (unpack, order fix, float64 dequant, float64 matmul)
+    for the workload's cases in order until ``seconds`` of CPU time are spent.
+    Value in the metric's unit (packed-weight GB/s)."""
+    import oracle as O
+    from synthetic import make_acts, make_layer_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    done, wbytes, spent = [], 0, 0.0
+    for c in cases:
+        Lw = make_layer_inputs(c)
+        for M in c.Ms:
+            x = make_acts(c, M)
+            t0 = time.perf_counter()
+            O.reference_linear(x, c.fmt, c.dtype, Lw["qweight"], Lw["qzeros"], Lw["scales"], c.group_size,
+                               g_idx=Lw["g_idx"])
+            dt = time.perf_counter() - t0
+            spent += dt
+            wbytes += c.K * c.N // 2
+            done.append(f"(K={c.K},N={c.N},M={M})")
+            if spent >= seconds:
+                break
+        if spent >= seconds:
+            break
+    return {"value": round(wbytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(done)} whole-layer oracle calls: " + " ".join(done), "seconds": round(spent, 2)}
+
+
+if __name__ == "__main__":
+    main()

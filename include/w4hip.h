@@ -1,0 +1,170 @@
+/*
+ * w4hip.h -- C ABI of libw4hip: weight-only INT4 group-quantized linear
+ * layers (AWQ / GPTQ, W4A16) on AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow the three-phase lifecycle of a quantized linear layer in
+ * the vLLM / SGLang designs: create the parameters (here: validate the layer
+ * and report buffer sizes; the caller allocates), post-process the weights
+ * once after loading (AWQ -> standard repack, then standard -> kernel tile
+ * repack), and apply the quantized GEMM on every forward pass.  See the
+ * SGLang quantization design page, section 1 (three hooks), and the vLLM
+ * "Quantized layer loading: AWQ / GPTQ / Marlin / fp8" page, sections
+ * "Responsibilities" and "Data flow".
+ *
+ * Conventions for every call:
+ *   - All buffers are owned by the caller.  The library never allocates or
+ *     frees memory, keeps no per-layer state and is thread-safe.
+ *   - Pointers named *_dev / weights / activations are device pointers;
+ *     descriptor and size pointers are host pointers.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued asynchronously on it; no call synchronizes.
+ *   - Arguments are validated on the host before any launch; an error
+ *     return means nothing was enqueued.  W4_ERR_HIP means a launch failed.
+ *   - Integers: int32 words hold eight 4-bit codes each ("packed words").
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef W4HIP_H
+#define W4HIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4_OK = 0,
+  W4_ERR_INVALID_ARGUMENT = 1, /* null / misaligned pointer, negative M, missing zeros or g_idx */
+  W4_ERR_UNSUPPORTED = 2,      /* shape, group size, dtype or device the kernels do not handle */
+  W4_ERR_WORKSPACE = 3,        /* workspace smaller than w4_workspace_size() */
+  W4_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} w4_status;
+
+typedef enum { W4_FP16 = 0, W4_BF16 = 1 } w4_dtype;
+
+/* Layer descriptor; the analogue of the MPLinearLayerConfig of the vLLM
+ * "Quantized layer loading" page ("Design motivation"): weight shape, group
+ * size, zero points, act-order, activation dtype.  4-bit weights only. */
+typedef struct {
+  int64_t K;               /* input features (rows of the weight)              */
+  int64_t N;               /* output features (columns of the weight)          */
+  int32_t group_size;      /* 32, 64, 128, or -1 = one group of K rows
+                              (per-channel; "Boundaries and failures")        */
+  int32_t has_zero_points; /* 0: symmetric, every zero point is 8              */
+  int32_t has_g_idx;       /* 1: GPTQ act-order, a g_idx[K] gives each row's group */
+  int32_t act_dtype;       /* w4_dtype of x, scales, bias and y               */
+} w4_layer;
+
+/* Byte sizes of the buffers of one layer (host-side arithmetic only). */
+typedef struct {
+  size_t awq_qweight;   /* int32 [K][N/8]   AWQ qweight (packed along N)          */
+  size_t qzeros;        /* int32 [G][N/8]   AWQ or standard zero words (0 if none) */
+  size_t scales;        /* act   [G][N]     scales as loaded                       */
+  size_t std_qweight;   /* int32 [K/8][N]   standard qweight (packed along K)      */
+  size_t tiled_qweight; /* int32 K*N/8      tile layout (see w4_repack_gptq)       */
+  size_t tiled_scales;  /* act   [N/16][G][16]                                      */
+  size_t tiled_qzeros;  /* int32 [N/16][G][2] (0 if no zero points)                */
+  size_t perm;          /* int32 [K] act-order row permutation (0 without g_idx)   */
+} w4_sizes_t;
+
+/* Validate a layer descriptor (analogue of the support check that raises in
+ * the vLLM "Boundaries and failures" section).  Returns
+ *   W4_ERR_INVALID_ARGUMENT  layer == NULL, K <= 0, N <= 0;
+ *   W4_ERR_UNSUPPORTED       group_size not in {-1, 32, 64, 128} (the group
+ *                            sizes listed in section 5.3 of the vLLM AWQ
+ *                            practice page), K % 128 != 0, N % 16 != 0,
+ *                            K % group_size != 0, act_dtype not fp16/bf16,
+ *                            has_g_idx with group_size == -1, K > 2^20 or
+ *                            N > 2^20.
+ * Host only; never touches the GPU. */
+w4_status w4_check_layer(const w4_layer* layer);
+
+/* Fill *out with the byte sizes of the layer's buffers.  Host only. */
+w4_status w4_sizes(const w4_layer* layer, w4_sizes_t* out);
+
+/* Bytes of scratch device memory w4a16_linear needs for M rows (0 when the
+ * chosen kernel needs none).  Host only. */
+w4_status w4_workspace_size(const w4_layer* layer, int64_t M, size_t* bytes);
+
+/* Name of the kernel w4a16_linear launches for M rows (the analogue of the
+ * "Using ... kernel" log line of the vLLM learning-book page, Q1), or
+ * "invalid" for a bad descriptor.  Static string; host only. */
+const char* w4_kernel_name(const w4_layer* layer, int64_t M);
+
+/* Static description of a status code. */
+const char* w4_status_str(w4_status s);
+
+/* AWQ -> standard repack (the vLLM AWQ practice page, section 5.1; the
+ * "Design motivation" section of the loading page).  Each AWQ word holds
+ * eight output columns, logical column j in nibble slot R[j] with
+ * R = [0,4,1,5,2,6,3,7]; the output packs eight input rows per word along K
+ * in the standard order (row 8r+i in slot i).
+ *   awq_qweight  int32 [K][N/8]  (device, 4-byte aligned)
+ *   awq_qzeros   int32 [G][N/8]  (device; AWQ always carries zero points)
+ *   std_qweight  int32 [K/8][N]  (device, 16-byte aligned) -- written
+ *   std_qzeros   int32 [G][N/8]  (device) -- written: same shape, standard
+ *                nibble order (column 8c+i in slot i)
+ * Out-of-place and re-runnable (a weight update re-runs it).  Requires
+ * layer->has_zero_points and !layer->has_g_idx; otherwise
+ * W4_ERR_UNSUPPORTED.  Bit-exact. */
+w4_status w4_repack_awq(const w4_layer* layer, const int32_t* awq_qweight, const int32_t* awq_qzeros,
+                        int32_t* std_qweight, int32_t* std_qzeros, void* stream);
+
+/* Standard -> gfx950 tile repack (the kernel-specific re-layout of the
+ * loading page's "Key files" / "Data flow"; act-order g_idx from its
+ * "Design motivation").
+ *   std_qweight    int32 [K/8][N]      (device)
+ *   std_qzeros     int32 [G][N/8]      (device; NULL iff !has_zero_points)
+ *   scales         act   [G][N]        (device)
+ *   g_idx          int32 [K]           (device; NULL iff !has_g_idx)
+ *   tiled_qweight  int32 [K*N/8]       (device, 16-byte aligned) -- written
+ *   tiled_scales   act   [N/16][G][16] (device) -- written
+ *   tiled_qzeros   int32 [N/16][G][2]  (device; NULL iff !has_zero_points) -- written
+ *   perm           int32 [K]           (device; NULL iff !has_g_idx) -- written
+ *   status_dev     int32 [1]           (device; may be NULL) -- written:
+ *                  bit 0 = a g_idx entry outside [0, G); bit 1 = some group
+ *                  does not own exactly group_size rows.  A nonzero status
+ *                  means the tiled buffers are not valid for w4a16_linear.
+ *                  perm always holds indices in [0, K).
+ * Layout (bit-exact): with act-order, rows are sorted stably by group
+ * (perm[k'] = original row of sorted row k'); a scale equal to zero is
+ * replaced by the previous group's stored scale (1.0 for group 0) and the
+ * codes of that group and column by its zero point; word [t][b][l][j]
+ * (t < N/16, b < K/128, l < 64, j < 4) holds column 16t + l%16 at sorted
+ * rows 128b + 32j + 8(l/16) + e, e = 0..7, K-offset e in nibble slot
+ * [0,4,1,5,2,6,3,7][e]. */
+w4_status w4_repack_gptq(const w4_layer* layer, const int32_t* std_qweight, const int32_t* std_qzeros,
+                         const void* scales, const int32_t* g_idx, int32_t* tiled_qweight,
+                         void* tiled_scales, int32_t* tiled_qzeros, int32_t* perm, int32_t* status_dev,
+                         void* stream);
+
+/* y = x * W + bias with W[k][n] = (q[k][n] - z[g(k)][n]) * s[g(k)][n]
+ * (dequantization of the vLLM AWQ practice page, section 5.3, fused into
+ * the GEMM as in the learning-book page, section 5.3), for the tiled
+ * buffers written by w4_repack_gptq.  fp32 accumulation; y rounded once
+ * (round to nearest even) to the activation dtype.
+ *   M              rows of x and y (M == 0: no launch, W4_OK)
+ *   x              act [M][K] row-major (device, 16-byte aligned)
+ *   tiled_qweight, tiled_scales, tiled_qzeros (NULL iff !has_zero_points),
+ *   perm (NULL iff !has_g_idx): as written by w4_repack_gptq
+ *   bias           act [N] (device) or NULL
+ *   y              act [M][N] row-major (device, 4-byte aligned) -- written
+ *   workspace      device scratch of >= w4_workspace_size() bytes (16-byte
+ *                  aligned), or NULL when that size is 0.  Its first 256-byte
+ *                  aligned part holds split-K arrival counters: the buffer
+ *                  must be zero-filled before its first use, and every
+ *                  completed call leaves those counters zero again, so one
+ *                  workspace can serve any sequence of calls on a stream.
+ *                  Calls that overlap in time must not share a workspace.
+ * Accuracy: within max|y - ref| <= 1e-2 (1 + |ref|) elementwise and
+ * relative Frobenius error <= 2e-3 of the float64 reference. */
+w4_status w4a16_linear(const w4_layer* layer, int64_t M, const void* x, const int32_t* tiled_qweight,
+                       const void* tiled_scales, const int32_t* tiled_qzeros, const int32_t* perm,
+                       const void* bias, void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4HIP_H */

@@ -1,0 +1,368 @@
+"""GPU parity of libw4hip against the CPU oracle (MI355X / gfx950).
+
+* Repacks must match the oracle bit for bit; outputs are pre-filled with
+  0x00 and with 0xFF and both runs must agree (no unwritten words).
+* GEMM outputs must satisfy the acceptance bound of the layer:
+  max |y - ref| <= 1e-2 (1 + |ref|) elementwise and
+  ||y - ref||_F / ||ref||_F <= 2e-3, against the float64 reference.
+  Small shapes are compared element by element; the full workload shapes, in
+  the launch configuration the benchmark times, on sampled outputs that the
+  oracle computes one by one.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from synthetic import (
+    CONFIGS, actorder_gidx, constant_words, make_acts, make_layer_inputs, normal_acts, random_words, seeded,
+    to_bf16_bits, uniform_scales,
+)
+from tests._gpu import act_dtype, filled, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+ELEM_TOL = 1e-2   # max |y - ref| <= ELEM_TOL * (1 + |ref|)
+FRO_TOL = 2e-3    # ||y - ref||_F / ||ref||_F <= FRO_TOL
+
+
+@pytest.fixture(scope="module")
+def W():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import weight_only_int4_gptq_amd as W
+    W.lib()
+    return W
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------
+# Repack: bit exact
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K,N", [(512, 256), (384, 48), (4096, 4096), (11008, 4096)])
+def test_repack_awq_bit_exact(W, K, N):
+    import torch
+    say(f"repack_awq K={K} N={N}")
+    G = K // 128
+    rng = seeded(101, K, N)
+    aw = random_words(rng, (K, N // 8))
+    az = random_words(rng, (G, N // 8))
+    ref_w, ref_z = O.awq_to_std(aw, az)
+    L = W.make_layer(K, N, 128, True, False, "fp16")
+    outs = []
+    for fill in (0x00, 0xFF):
+        sw = filled((K // 8, N), torch.int32, fill)
+        sz = filled((G, N // 8), torch.int32, fill)
+        W.w4_repack_awq(L, to_dev(aw), to_dev(az), sw, sz)
+        _sync()
+        outs.append((to_host(sw), to_host(sz)))
+    for sw, sz in outs:
+        assert np.array_equal(sw, ref_w)
+        assert np.array_equal(sz, ref_z)
+
+
+REPACK_VARIANTS = [
+    # (name, K, N, group_size, has_zeros, has_gidx, dtype, zero_scales)
+    ("fp16-g128-z", 512, 256, 128, True, False, "fp16", False),
+    ("bf16-g128-sym", 384, 48, 128, False, False, "bf16", False),
+    ("fp16-g128-z-act", 512, 64, 128, True, True, "fp16", False),
+    ("fp16-g32-z", 384, 48, 32, True, False, "fp16", False),
+    ("bf16-g64-z", 384, 48, 64, True, False, "bf16", False),
+    ("fp16-ch-z", 384, 48, -1, True, False, "fp16", False),
+    ("bf16-g64-sym-act", 512, 32, 64, False, True, "bf16", False),
+    ("fp16-g64-z-zeroscales", 384, 48, 64, True, False, "fp16", True),
+    ("bf16-g128-sym-zeroscales-act", 512, 32, 128, False, True, "bf16", True),
+    ("fp16-g128-z-act-8192", 8192, 256, 128, True, True, "fp16", False),
+]
+
+
+def _std_layer_inputs(K, N, gs, has_z, has_g, dtype, zero_scales, seed=7):
+    G = 1 if gs == -1 else K // gs
+    rng = seeded(202, K, N, G, seed)
+    sw = random_words(rng, (K // 8, N))
+    sz = random_words(rng, (G, N // 8)) if has_z else None
+    lo, hi = (0.002, 0.02) if dtype == "fp16" else (0.001, 0.01)
+    s = uniform_scales(rng, (G, N), lo, hi, dtype)
+    if zero_scales:
+        idx = rng.choice(G * N, size=max(1, G * N // 7), replace=False)
+        s.reshape(-1)[idx] = 0
+        if dtype == "fp16":
+            s.reshape(-1)[idx[:3]] = np.float16(-0.0)
+        else:
+            s.reshape(-1)[idx[:3]] = 0x8000
+        s[0, 0] = 0
+    gi = actorder_gidx(rng, K, gs) if has_g else None
+    return sw, sz, s, gi
+
+
+@pytest.mark.parametrize("v", REPACK_VARIANTS, ids=[v[0] for v in REPACK_VARIANTS])
+def test_repack_gptq_bit_exact(W, v):
+    import torch
+    name, K, N, gs, has_z, has_g, dtype, zs = v
+    say(f"repack_gptq {name}")
+    G = 1 if gs == -1 else K // gs
+    sw, sz, s, gi = _std_layer_inputs(K, N, gs, has_z, has_g, dtype, zs)
+    ref = O.tile_layout(sw, sz, s, gs, dtype, g_idx=gi)
+    L = W.make_layer(K, N, gs, has_z, has_g, dtype)
+    outs = []
+    for fill in (0x00, 0xFF):
+        tw = filled((K * N // 8,), torch.int32, fill)
+        ts = filled((N // 16, G, 16), act_dtype(dtype), fill)
+        tz = filled((N // 16, G, 2), torch.int32, fill) if has_z else None
+        pm = filled((K,), torch.int32, fill) if has_g else None
+        st = filled((1,), torch.int32, fill)
+        W.w4_repack_gptq(L, to_dev(sw), to_dev(sz) if has_z else None, to_dev(s), to_dev(gi) if has_g else None,
+                         tw, ts, tz, pm, st)
+        _sync()
+        outs.append((to_host(tw), to_host(ts), to_host(tz) if has_z else None, to_host(pm) if has_g else None,
+                     int(to_host(st)[0])))
+    for tw, ts, tz, pm, st in outs:
+        assert st == 0
+        assert np.array_equal(tw, ref["qweight"])
+        assert np.array_equal(ts.view(np.uint16), ref["scales"])
+        if has_z:
+            assert np.array_equal(tz, ref["zeros"])
+        if has_g:
+            assert np.array_equal(pm, ref["perm"])
+
+
+@pytest.mark.parametrize("case", ["ok", "out_of_range", "negative", "unequal", "both"])
+def test_actorder_status_and_perm_range(W, case):
+    import torch
+    say(f"actorder status {case}")
+    K, N, gs = 512, 32, 128
+    G = K // gs
+    sw, sz, s, gi = _std_layer_inputs(K, N, gs, True, True, "fp16", False)
+    gi = gi.copy()
+    if case == "out_of_range":
+        gi[5] = G
+    elif case == "negative":
+        gi[300] = -2
+    elif case == "unequal":
+        gi[gi == 1] = 2
+    elif case == "both":
+        gi[0], gi[1] = 7, 0
+    expect = O.gidx_status(gi, G, gs)
+    L = W.make_layer(K, N, gs, True, True, "fp16")
+    tw = torch.empty((K * N // 8,), dtype=torch.int32, device="cuda")
+    ts = torch.empty((N // 16, G, 16), dtype=torch.float16, device="cuda")
+    tz = torch.empty((N // 16, G, 2), dtype=torch.int32, device="cuda")
+    pm = filled((K,), torch.int32, 0xFF)
+    st = filled((1,), torch.int32, 0xFF)
+    W.w4_repack_gptq(L, to_dev(sw), to_dev(sz), to_dev(s), to_dev(gi), tw, ts, tz, pm, st)
+    _sync()
+    assert int(to_host(st)[0]) == expect
+    p = to_host(pm)
+    assert ((p >= 0) & (p < K)).all()
+    if expect == 0:
+        assert np.array_equal(p, O.actorder_perm(gi))
+
+
+# ----------------------------------------------------------------------------
+# GEMM: small shapes, element by element
+# ----------------------------------------------------------------------------
+
+def _prepare(W, fmt, K, N, gs, has_z, has_g, dtype, qweight, qzeros, scales, g_idx):
+    Lyr = W.W4A16Linear(K, N, gs, has_z, has_g, dtype, fmt)
+    Lyr.process_weights_after_loading(to_dev(qweight), to_dev(qzeros) if has_z else None, to_dev(scales),
+                                      to_dev(g_idx) if has_g else None)
+    return Lyr
+
+
+def _run_linear(W, Lyr, x, bias=None, guard_rows=16, fill=0x7F):
+    """Run w4a16_linear into the first M rows of a pre-filled buffer; return
+    (y, guard rows after the call)."""
+    import torch
+    M = x.shape[0]
+    buf = filled((M + guard_rows, Lyr.N), act_dtype(Lyr.dtype), fill)
+    y = buf[:M]
+    Lyr.apply(to_dev(x), to_dev(bias) if bias is not None else None, out=y)
+    _sync()
+    return to_host(y), to_host(buf[M:])
+
+
+def _rounding_floor(ref, dtype):
+    """rel-Frobenius error of the correctly rounded reference itself."""
+    r32 = ref.astype(np.float32)
+    rr = r32.astype(np.float16).astype(np.float64) if dtype == "fp16" else O.bf16_to_f64(to_bf16_bits(r32))
+    return O.check(rr, ref)["rel_fro"]
+
+
+def _assert_close(y_bits, ref, dtype, what):
+    """Acceptance bound of the layer.  The Frobenius bound is never made
+    stricter than the error of the correctly rounded reference: on a few
+    hundred bf16 outputs that rounding alone can exceed 2e-3."""
+    y = O.act_to_f64(y_bits, dtype)
+    floor = _rounding_floor(ref, dtype)
+    fro = max(FRO_TOL, 1.05 * floor)
+    r = O.check(y, ref, ELEM_TOL, fro)
+    say(f"  {what}: max_ratio={r['max_ratio']:.3e} rel_fro={r['rel_fro']:.3e} (rounding floor {floor:.3e})")
+    assert r["ok"], (what, r, floor)
+    return r
+
+
+def test_linear_tiny_workload(W):
+    c = CONFIGS[0]
+    Lw = make_layer_inputs(c)
+    Lyr = _prepare(W, "awq", c.K, c.N, c.group_size, True, False, "fp16", Lw["qweight"], Lw["qzeros"],
+                   Lw["scales"], None)
+    for M in c.Ms:
+        say(f"tiny M={M} kernel={Lyr.kernel_name(M)}")
+        x = make_acts(c, M)
+        ref = O.reference_linear(x, "awq", "fp16", Lw["qweight"], Lw["qzeros"], Lw["scales"], c.group_size)
+        y, guard = _run_linear(W, Lyr, x)
+        _assert_close(y, ref, "fp16", f"tiny M={M}")
+        assert (guard.view(np.uint16) == 0x7F7F).all()
+
+
+LINEAR_VARIANTS = [
+    # (name, fmt, K, N, group_size, has_zeros, has_gidx, dtype, with_bias)
+    ("awq-fp16-g128", "awq", 384, 272, 128, True, False, "fp16", False),
+    ("awq-fp16-g128-bias", "awq", 384, 272, 128, True, False, "fp16", True),
+    ("std-bf16-g128-sym", "std", 384, 272, 128, False, False, "bf16", False),
+    ("std-bf16-g128-sym-bias", "std", 384, 272, 128, False, False, "bf16", True),
+    ("std-fp16-g128-z-act", "std", 512, 272, 128, True, True, "fp16", False),
+    ("std-fp16-g32-z", "std", 384, 272, 32, True, False, "fp16", False),
+    ("std-bf16-g64-z", "std", 384, 272, 64, True, False, "bf16", False),
+    ("std-fp16-ch-z", "std", 384, 272, -1, True, False, "fp16", False),
+    ("std-bf16-ch-sym", "std", 384, 272, -1, False, False, "bf16", False),
+    ("std-bf16-g64-sym-act", "std", 512, 272, 64, False, True, "bf16", True),
+]
+LINEAR_MS = (1, 3, 16, 17, 33, 64, 70, 130)
+
+
+@pytest.mark.parametrize("v", LINEAR_VARIANTS, ids=[v[0] for v in LINEAR_VARIANTS])
+def test_linear_small_shapes_all_m(W, v):
+    name, fmt, K, N, gs, has_z, has_g, dtype, with_bias = v
+    G = 1 if gs == -1 else K // gs
+    rng = seeded(303, K, N, G, int(has_z), int(has_g), len(name))
+    lo, hi = (0.002, 0.02) if dtype == "fp16" else (0.001, 0.01)
+    qweight = random_words(rng, (K, N // 8) if fmt == "awq" else (K // 8, N))
+    qzeros = random_words(rng, (G, N // 8)) if has_z else None
+    scales = uniform_scales(rng, (G, N), lo, hi, dtype)
+    g_idx = actorder_gidx(rng, K, gs) if has_g else None
+    bias = uniform_scales(rng, (N,), -1.0, 1.0, dtype) if with_bias else None
+    Lyr = _prepare(W, fmt, K, N, gs, has_z, has_g, dtype, qweight, qzeros, scales, g_idx)
+    for M in LINEAR_MS:
+        say(f"{name} M={M} kernel={Lyr.kernel_name(M)}")
+        x = normal_acts(seeded(304, M, K), (M, K), dtype)
+        ref = O.reference_linear(x, fmt, dtype, qweight, qzeros, scales, gs, g_idx=g_idx, bias=bias)
+        ys = []
+        for fill in (0x00, 0xFF):
+            y, guard = _run_linear(W, Lyr, x, bias, fill=fill)
+            assert (guard.view(np.uint8) == fill).all(), "write past row M"
+            ys.append(y)
+        assert np.array_equal(ys[0].view(np.uint16), ys[1].view(np.uint16)), "unwritten outputs"
+        _assert_close(ys[0], ref, dtype, f"{name} M={M}")
+
+
+def test_linear_closed_forms(W):
+    # constant codes c, zero z0, scale s0: y[m, n] = (c - z0) s0 sum_k x[m, k]
+    K, N, gs = 512, 64, 128
+    G = K // gs
+    for c, z0, dtype in ((13, 2, "fp16"), (0, 15, "bf16"), (9, 9, "fp16")):
+        say(f"closed form c={c} z0={z0} {dtype}")
+        qw = constant_words((K // 8, N), c)
+        qz = constant_words((G, N // 8), z0)
+        s = np.full((G, N), 0.0078125, dtype=np.float16) if dtype == "fp16" else \
+            np.full((G, N), 0x3C00, dtype=np.uint16)  # bf16 0x3C00 = 2^-7
+        Lyr = _prepare(W, "std", K, N, gs, True, False, dtype, qw, qz, s, None)
+        x = normal_acts(seeded(5, c), (5, K), dtype)
+        xs = O.act_to_f64(x, dtype)
+        ref = np.repeat(((c - z0) * 0.0078125 * xs.sum(axis=1))[:, None], N, axis=1)
+        y, _ = _run_linear(W, Lyr, x)
+        _assert_close(y, ref, dtype, f"closed form c={c} z0={z0}")
+        if c == z0:
+            assert (O.act_to_f64(y, dtype) == 0).all()
+    # one-hot rows select dequantized weight rows
+    say("one-hot rows")
+    rng = seeded(6)
+    qw = random_words(rng, (K // 8, N))
+    qz = random_words(rng, (G, N // 8))
+    s = uniform_scales(rng, (G, N), 0.002, 0.02, "fp16")
+    Lyr = _prepare(W, "std", K, N, gs, True, False, "fp16", qw, qz, s, None)
+    ks = np.array([0, 1, 127, 128, 300, 511])
+    x = np.zeros((len(ks), K), dtype=np.float16)
+    x[np.arange(len(ks)), ks] = 1.0
+    y, _ = _run_linear(W, Lyr, x)
+    q, z = O.codes_from_inputs("std", qw, qz)
+    Wd = O.dequant(q, z, O.half_to_f64(s), O.group_index(K, gs))
+    expect = Wd[ks].astype(np.float16)       # one exact product, rounded once to fp16
+    assert np.array_equal(y.view(np.uint16), expect.view(np.uint16))
+
+
+def test_linear_zero_scales_give_bias(W):
+    K, N, gs = 384, 48, 64
+    say("zero scales -> bias")
+    sw, sz, s, _ = _std_layer_inputs(K, N, gs, True, False, "fp16", False)
+    s[:] = 0
+    bias = uniform_scales(seeded(8), (N,), -1, 1, "fp16")
+    Lyr = _prepare(W, "std", K, N, gs, True, False, "fp16", sw, sz, s, None)
+    x = normal_acts(seeded(9), (7, K), "fp16")
+    y, _ = _run_linear(W, Lyr, x, bias)
+    assert np.array_equal(y.view(np.uint16), np.repeat(bias[None, :], 7, axis=0).view(np.uint16))
+
+
+def test_linear_m_zero_is_a_no_op(W):
+    import torch
+    say("M = 0")
+    c = CONFIGS[0]
+    Lw = make_layer_inputs(c)
+    Lyr = _prepare(W, "awq", c.K, c.N, c.group_size, True, False, "fp16", Lw["qweight"], Lw["qzeros"],
+                   Lw["scales"], None)
+    y = filled((1, c.N), torch.float16, 0x5A)
+    t = Lyr.tiled
+    W.w4a16_linear(Lyr.layer, 0, to_dev(np.zeros((1, c.K), np.float16)), t["qweight"], t["scales"], t["qzeros"],
+                   None, None, y)
+    _sync()
+    assert (to_host(y).view(np.uint8) == 0x5A).all()
+
+
+def test_loaded_library_is_in_tree(W):
+    lib_path = os.path.realpath(W.lib()._name)
+    pkg = os.path.realpath(os.path.join(os.path.dirname(__file__), "..", "weight_only_int4_gptq_amd"))
+    assert lib_path.startswith(pkg)
+
+
+# ----------------------------------------------------------------------------
+# GEMM: every workload shape at full size, sampled outputs
+# ----------------------------------------------------------------------------
+
+_FULL = [(c, M) for c in CONFIGS for M in c.Ms]
+_cache = {}
+
+
+def _full_layer(W, c):
+    if c.label not in _cache:
+        _cache.clear()
+        import torch
+        torch.cuda.empty_cache()
+        Lw = make_layer_inputs(c)
+        Lyr = _prepare(W, c.fmt, c.K, c.N, c.group_size, c.has_zeros, c.has_gidx, c.dtype, Lw["qweight"],
+                       Lw["qzeros"], Lw["scales"], Lw["g_idx"])
+        _cache[c.label] = (Lw, Lyr)
+    return _cache[c.label]
+
+
+@pytest.mark.parametrize("c,M", _FULL, ids=[f"{c.label}-M{M}" for c, M in _FULL])
+def test_linear_full_size_sampled(W, c, M):
+    say(f"full {c.label} M={M}")
+    Lw, Lyr = _full_layer(W, c)
+    say(f"  kernel={Lyr.kernel_name(M)}")
+    x = make_acts(c, M)
+    y, _ = _run_linear(W, Lyr, x, guard_rows=1)
+    yv = O.act_to_f64(y, c.dtype)
+    assert np.isfinite(yv).all()
+    rng = seeded(404, c.cfg_id, M, c.K, c.N)
+    ns = 1024
+    rows = np.concatenate([[0, M - 1], rng.integers(0, M, size=ns - 2)])
+    cols = np.concatenate([[0, c.N - 1], rng.integers(0, c.N, size=ns - 2)])
+    ref = O.reference_entries(x, c.fmt, c.dtype, Lw["qweight"], Lw["qzeros"], Lw["scales"], c.group_size, rows,
+                              cols, g_idx=Lw["g_idx"])
+    _assert_close(y[rows, cols], ref, c.dtype, f"{c.label} M={M} (sampled {ns})")

@@ -1,0 +1,126 @@
+"""Host-side checks of libw4hip that need no GPU: the library loads, exports
+every call include/w4hip.h declares, and rejects bad arguments before any
+device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4hip.h")
+
+
+@pytest.fixture(scope="module")
+def W():
+    import weight_only_int4_gptq_amd as W
+    from weight_only_int4_gptq_amd import _abi
+    if not os.path.exists(_abi._LIB_PATH):
+        # CPU-only convenience: cross-compile in-tree when nothing is built yet.
+        from weight_only_int4_gptq_amd import build
+        build.build()
+    W.lib()
+    return W
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:w4_status|const\s+char\s*\*)\s*(w4\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_lifecycle_calls():
+    names = declared_functions()
+    for n in ("w4_check_layer", "w4_sizes", "w4_workspace_size", "w4_kernel_name", "w4_status_str",
+              "w4_repack_awq", "w4_repack_gptq", "w4a16_linear"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(W):
+    L = W.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_check_layer_status_codes(W):
+    ok = W.make_layer(512, 256, 128, True, False, "fp16")
+    assert W.w4_check_layer(ok) == W.W4_OK
+    assert W.lib().w4_check_layer(None) == W.W4_ERR_INVALID_ARGUMENT
+    bad = [
+        (dict(K=0), W.W4_ERR_INVALID_ARGUMENT), (dict(N=-16), W.W4_ERR_INVALID_ARGUMENT),
+        (dict(group_size=16), W.W4_ERR_UNSUPPORTED), (dict(group_size=256), W.W4_ERR_UNSUPPORTED),
+        (dict(group_size=0), W.W4_ERR_UNSUPPORTED), (dict(K=200), W.W4_ERR_UNSUPPORTED),
+        (dict(N=24), W.W4_ERR_UNSUPPORTED), (dict(K=2 ** 21), W.W4_ERR_UNSUPPORTED),
+        (dict(group_size=-1, has_g_idx=True), W.W4_ERR_UNSUPPORTED), (dict(dtype=2), W.W4_ERR_UNSUPPORTED),
+    ]
+    for over, expect in bad:
+        kw = dict(K=512, N=256, group_size=128, has_zero_points=True, has_g_idx=False, dtype="fp16")
+        kw.update(over)
+        assert W.w4_check_layer(W.make_layer(**kw)) == expect, over
+    for gs in (-1, 32, 64, 128):
+        assert W.w4_check_layer(W.make_layer(384, 48, gs, False, False, "bf16")) == W.W4_OK
+
+
+def test_sizes_of_the_tiny_layer(W):
+    s = W.w4_sizes(W.make_layer(512, 256, 128, True, False, "fp16"))
+    assert s == dict(awq_qweight=512 * 32 * 4, qzeros=4 * 32 * 4, scales=4 * 256 * 2, std_qweight=64 * 256 * 4,
+                     tiled_qweight=512 * 256 // 2, tiled_scales=4 * 256 * 2, tiled_qzeros=16 * 4 * 2 * 4, perm=0)
+    s = W.w4_sizes(W.make_layer(8192, 8192, 128, True, True, "fp16"))
+    assert s["perm"] == 8192 * 4
+    s = W.w4_sizes(W.make_layer(8192, 8192, -1, False, False, "bf16"))
+    assert s["scales"] == 8192 * 2 and s["qzeros"] == 0 and s["tiled_qzeros"] == 0
+    with pytest.raises(W.W4Error):
+        W.w4_sizes(W.make_layer(100, 256))
+
+
+def test_workspace_and_kernel_name(W):
+    L = W.make_layer(4096, 4096)
+    assert W.w4_workspace_size(L, 0) == 0
+    assert W.w4_workspace_size(L, 16) >= 0
+    with pytest.raises(W.W4Error):
+        W.w4_workspace_size(L, -1)
+    assert W.w4_kernel_name(L, 0) == "none"
+    assert W.w4_kernel_name(L, -3) == "invalid"
+    assert W.w4_kernel_name(W.make_layer(100, 16), 1) == "invalid"
+    assert W.w4_kernel_name(L, 1).startswith("w4_")
+    for s in range(5):
+        assert W.w4_status_str(s)
+    assert W.w4_status_str(99) == "unknown status"
+
+
+def _lin(W, L, M, x=16, qw=16, sc=16, qz=16, perm=None, bias=None, y=16, ws=None, ws_bytes=0):
+    return W.lib().w4a16_linear(ctypes.byref(L), M, x, qw, sc, qz, perm, bias, y, ws, ws_bytes, None)
+
+
+def test_linear_rejects_bad_arguments_before_any_launch(W):
+    L = W.make_layer(512, 256, 128, True, False, "fp16")
+    assert _lin(W, L, -1) == W.W4_ERR_INVALID_ARGUMENT
+    assert _lin(W, L, 1, x=None) == W.W4_ERR_INVALID_ARGUMENT
+    assert _lin(W, L, 1, y=None) == W.W4_ERR_INVALID_ARGUMENT
+    assert _lin(W, L, 1, qz=None) == W.W4_ERR_INVALID_ARGUMENT          # zero points declared, none given
+    assert _lin(W, L, 1, x=24) == W.W4_ERR_INVALID_ARGUMENT             # x not 16-byte aligned
+    assert _lin(W, L, 1, qw=8) == W.W4_ERR_INVALID_ARGUMENT
+    assert _lin(W, L, 1, perm=16) == W.W4_ERR_INVALID_ARGUMENT          # perm without act-order
+    assert _lin(W, L, 2 ** 25) == W.W4_ERR_UNSUPPORTED
+    assert _lin(W, L, 0) == W.W4_OK                                     # M == 0: nothing to do
+    La = W.make_layer(512, 256, 128, True, True, "fp16")
+    assert _lin(W, La, 1) == W.W4_ERR_INVALID_ARGUMENT                  # act-order needs perm
+    Ls = W.make_layer(512, 256, 128, False, False, "bf16")
+    assert _lin(W, Ls, 1) == W.W4_ERR_INVALID_ARGUMENT                  # zeros given for a symmetric layer
+    bad = W.make_layer(100, 256)
+    assert _lin(W, bad, 1) == W.W4_ERR_UNSUPPORTED
+
+
+def test_repacks_reject_bad_arguments(W):
+    lib = W.lib()
+    L = W.make_layer(512, 256, 128, True, False, "fp16")
+    sym = W.make_layer(512, 256, 128, False, False, "fp16")
+    assert lib.w4_repack_awq(ctypes.byref(sym), 16, 16, 16, 16, None) == W.W4_ERR_UNSUPPORTED
+    assert lib.w4_repack_awq(ctypes.byref(L), None, 16, 16, 16, None) == W.W4_ERR_INVALID_ARGUMENT
+    assert lib.w4_repack_awq(ctypes.byref(L), 16, 16, 20, 16, None) == W.W4_ERR_INVALID_ARGUMENT
+    g = lib.w4_repack_gptq
+    assert g(ctypes.byref(L), 16, None, 16, None, 16, 16, 16, None, None, None) == W.W4_ERR_INVALID_ARGUMENT
+    assert g(ctypes.byref(sym), 16, 16, 16, None, 16, 16, None, None, None, None) == W.W4_ERR_INVALID_ARGUMENT
+    act = W.make_layer(512, 256, 128, True, True, "fp16")
+    assert g(ctypes.byref(act), 16, 16, 16, None, 16, 16, 16, 16, None, None) == W.W4_ERR_INVALID_ARGUMENT
+    assert g(ctypes.byref(act), 16, 16, 16, 16, 16, 16, 16, 20, None, None) == W.W4_ERR_INVALID_ARGUMENT

@@ -1,0 +1,67 @@
+// Internal declarations shared by the libw4hip translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "w4hip.h"
+
+namespace w4 {
+
+// Tile geometry of the kernel weight layout: a block is 16 output columns
+// (one "strip") by 128 input rows, 1 KiB of packed codes; each of the 64
+// lanes of a wave owns 16 contiguous bytes (4 words) of a block.
+constexpr int kTileN = 16;
+constexpr int kTileK = 128;
+constexpr int kWordsPerBlock = kTileN * kTileK / 8;  // 256
+
+struct Shape {
+  int64_t K, N;
+  int gs;  // effective group size (K for per-channel)
+  int G;   // number of groups
+  bool bf16, has_z, has_perm;
+};
+
+inline Shape shape_of(const w4_layer* L) {
+  Shape s;
+  s.K = L->K;
+  s.N = L->N;
+  s.gs = L->group_size == -1 ? (int)L->K : L->group_size;
+  s.G = (int)(L->K / s.gs);
+  s.bf16 = L->act_dtype == W4_BF16;
+  s.has_z = L->has_zero_points != 0;
+  s.has_perm = L->has_g_idx != 0;
+  return s;
+}
+
+// ---- repack launchers (w4_repack.hip) ----
+hipError_t launch_awq_to_std(const Shape& s, const int32_t* awq_w, const int32_t* awq_z, int32_t* std_w,
+                             int32_t* std_z, hipStream_t st);
+hipError_t launch_actorder_perm(const Shape& s, const int32_t* g_idx, int32_t* perm, int32_t* status,
+                                hipStream_t st);
+hipError_t launch_status_zero(int32_t* status, hipStream_t st);
+hipError_t launch_tile(const Shape& s, const int32_t* std_w, const int32_t* std_z, const uint16_t* scales,
+                       const int32_t* perm, int32_t* tiled_w, uint16_t* tiled_s, int32_t* tiled_z,
+                       hipStream_t st);
+
+// ---- GEMM (w4_gemm.hip) ----
+enum class GemmKind { kSkinny, kWide };
+
+struct GemmPlan {
+  GemmKind kind;
+  int mt;        // 16-row M tiles per wave (skinny kernel)
+  int nb;        // strips per workgroup
+  int kw;        // waves splitting K inside a workgroup
+  int u;         // 128-row blocks per load run
+  int ks;        // workgroups splitting K (split-K fix-up through the workspace)
+  const char* name;
+};
+
+GemmPlan plan_gemm(const Shape& s, int64_t M);
+size_t gemm_workspace_bytes(const Shape& s, int64_t M);
+hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* tiled_w, const void* tiled_s,
+                       const int32_t* tiled_z, const int32_t* perm, const void* bias, void* y, void* ws,
+                       hipStream_t st);
+
+}  // namespace w4

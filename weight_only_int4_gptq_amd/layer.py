@@ -1,0 +1,114 @@
+"""create_weights / process_weights_after_loading / apply for one W4A16
+linear layer (the three-phase split of the SGLang quantization design page,
+section 1, and of the vLLM loading page, "Responsibilities").
+
+torch is used only to allocate device memory and to name the current stream;
+every step of the computation runs in libw4hip's HIP kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _abi as A
+
+_TORCH_DTYPE = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+class W4A16Linear:
+    """One weight-only INT4 linear layer on the current CUDA (HIP) device.
+
+    fmt "awq": checkpoint qweight int32 [K, N/8] packed along N in the AWQ
+    order (the vLLM loading page, "Data flow"); fmt "std": standard/GPTQ
+    qweight int32 [K/8, N].  qzeros int32 [G, N/8] (absent when symmetric),
+    scales [G, N] in the activation dtype, g_idx int32 [K] with act-order.
+    """
+
+    def __init__(self, K: int, N: int, group_size: int = 128, has_zero_points: bool = True,
+                 has_g_idx: bool = False, dtype: str = "fp16", fmt: str = "awq", device="cuda"):
+        if fmt not in ("awq", "std"):
+            raise ValueError(fmt)
+        self.layer = A.make_layer(K, N, group_size, has_zero_points, has_g_idx, dtype)
+        st = A.w4_check_layer(self.layer)
+        if st != A.W4_OK:
+            raise A.W4Error("w4_check_layer", st, A.w4_status_str(st))
+        self.K, self.N, self.group_size, self.dtype, self.fmt = K, N, group_size, dtype, fmt
+        self.has_zero_points, self.has_g_idx = has_zero_points, has_g_idx
+        self.G = 1 if group_size == -1 else K // group_size
+        self.device = torch.device(device)
+        self.sizes = A.w4_sizes(self.layer)
+        self.tiled = None
+
+    # -- create_weights ----------------------------------------------------
+    def create_weights(self) -> dict:
+        """Empty checkpoint parameters with the shapes of the chosen format."""
+        d, i32 = self.device, torch.int32
+        K, N, G = self.K, self.N, self.G
+        qweight = torch.empty((K, N // 8) if self.fmt == "awq" else (K // 8, N), dtype=i32, device=d)
+        return {
+            "qweight": qweight,
+            "qzeros": torch.empty((G, N // 8), dtype=i32, device=d) if self.has_zero_points else None,
+            "scales": torch.empty((G, N), dtype=_TORCH_DTYPE[self.dtype], device=d),
+            "g_idx": torch.empty((K,), dtype=i32, device=d) if self.has_g_idx else None,
+        }
+
+    # -- process_weights_after_loading -------------------------------------
+    def process_weights_after_loading(self, qweight, qzeros, scales, g_idx=None, stream=None,
+                                      keep_standard: bool = False) -> dict:
+        """AWQ -> standard (fmt "awq") then standard -> tile layout.  Re-runnable.
+        With act-order the g_idx status word is read back once and a bad
+        g_idx raises ValueError."""
+        d, i32 = self.device, torch.int32
+        K, N, G = self.K, self.N, self.G
+        std_w, std_z = qweight, qzeros
+        if self.fmt == "awq":
+            std_w = torch.empty((K // 8, N), dtype=i32, device=d)
+            std_z = torch.empty((G, N // 8), dtype=i32, device=d)
+            A.w4_repack_awq(self.layer, qweight, qzeros, std_w, std_z, stream)
+        tiled = {
+            "qweight": torch.empty((K * N // 8,), dtype=i32, device=d),
+            "scales": torch.empty((N // 16, G, 16), dtype=_TORCH_DTYPE[self.dtype], device=d),
+            "qzeros": torch.empty((N // 16, G, 2), dtype=i32, device=d) if self.has_zero_points else None,
+            "perm": torch.empty((K,), dtype=i32, device=d) if self.has_g_idx else None,
+        }
+        status = torch.empty((1,), dtype=i32, device=d) if self.has_g_idx else None
+        A.w4_repack_gptq(self.layer, std_w, std_z, scales, g_idx, tiled["qweight"], tiled["scales"],
+                         tiled["qzeros"], tiled["perm"], status, stream)
+        if status is not None:
+            st = int(status.cpu().item())
+            if st != 0:
+                raise ValueError(f"invalid g_idx (status bits {st:#x}: 1 = out of range, 2 = group size != "
+                                 f"{self.group_size})")
+        if keep_standard:
+            tiled["std_qweight"], tiled["std_qzeros"] = std_w, std_z
+        self.tiled = tiled
+        return tiled
+
+    # -- apply -------------------------------------------------------------
+    def apply(self, x: torch.Tensor, bias=None, out=None, stream=None) -> torch.Tensor:
+        """y = x W + bias; x [..., K] in the activation dtype, leading dims flattened."""
+        if self.tiled is None:
+            raise RuntimeError("process_weights_after_loading has not run")
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, self.K)
+        if not x2.is_contiguous():
+            x2 = x2.contiguous()
+        M = x2.shape[0]
+        y = out if out is not None else torch.empty((M, self.N), dtype=x.dtype, device=x.device)
+        ws_bytes = A.w4_workspace_size(self.layer, M)
+        ws = self._workspace(ws_bytes, x.device) if ws_bytes else None
+        t = self.tiled
+        A.w4a16_linear(self.layer, M, x2, t["qweight"], t["scales"], t["qzeros"], t["perm"], bias, y, ws, ws_bytes,
+                       stream)
+        return y.reshape(*lead, self.N)
+
+    def _workspace(self, nbytes: int, device) -> "torch.Tensor":
+        """A zero-filled scratch buffer of at least nbytes, kept for later
+        calls (the library leaves its split-K counters zero after each call)."""
+        ws = getattr(self, "_ws", None)
+        if ws is None or ws.numel() < nbytes or ws.device != torch.device(device):
+            ws = torch.zeros((nbytes,), dtype=torch.uint8, device=device)
+            self._ws = ws
+        return ws
+
+    def kernel_name(self, M: int) -> str:
+        return A.w4_kernel_name(self.layer, M)
