@@ -257,22 +257,23 @@ def reference_entries(x, fmt, dtype, qweight, qzeros, scales, group_size, rows, 
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
     s = act_to_f64(scales, dtype)
-    xs = act_to_f64(x, dtype)
+    uniq, where = np.unique(rows, return_inverse=True)
+    xs = act_to_f64(np.asarray(x)[uniq], dtype)          # only the sampled rows
     K = xs.shape[1]
     grp = group_index(K, group_size, g_idx)
-    qw = u32(qweight)
+    qw = np.asarray(qweight)
     out = np.empty(rows.shape[0], dtype=np.float64)
-    for i, (m, n) in enumerate(zip(rows.tolist(), cols.tolist())):
+    for i, (mi, n) in enumerate(zip(where.tolist(), cols.tolist())):
         if fmt == "awq":
-            qcol = (qw[:, n // 8] >> (4 * AWQ_REVERSE_ORDER[n % 8])) & 0xF
+            qcol = (u32(qw[:, n // 8]) >> (4 * AWQ_REVERSE_ORDER[n % 8])) & 0xF
             zcol = None if qzeros is None else (u32(qzeros)[:, n // 8] >> (4 * AWQ_REVERSE_ORDER[n % 8])) & 0xF
         else:
             k = np.arange(K)
-            qcol = (qw[k // 8, n] >> (4 * (k % 8))) & 0xF
+            qcol = (u32(qw[:, n])[k // 8] >> (4 * (k % 8))) & 0xF
             zcol = None if qzeros is None else (u32(qzeros)[:, n // 8] >> (4 * (n % 8))) & 0xF
         zk = 8 if zcol is None else zcol[grp]
         wcol = (qcol - zk).astype(np.float64) * s[grp, n]
-        out[i] = float(np.dot(xs[m], wcol))
+        out[i] = float(np.dot(xs[mi], wcol))
         if bias is not None:
             out[i] += float(act_to_f64(bias, dtype)[n])
     return out
