@@ -55,6 +55,7 @@ struct GemmPlan {
   int kw;        // waves splitting K inside a workgroup
   int u;         // 128-row blocks per load run
   int ks;        // workgroups splitting K (split-K fix-up through the workspace)
+  bool xl;       // activations staged in LDS
   const char* name;
 };
 
