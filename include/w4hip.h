@@ -151,12 +151,10 @@ w4_status w4_repack_gptq(const w4_layer* layer, const int32_t* std_qweight, cons
  *   bias           act [N] (device) or NULL
  *   y              act [M][N] row-major (device, 4-byte aligned) -- written
  *   workspace      device scratch of >= w4_workspace_size() bytes (16-byte
- *                  aligned), or NULL when that size is 0.  Its first 256-byte
- *                  aligned part holds split-K arrival counters: the buffer
- *                  must be zero-filled before its first use, and every
- *                  completed call leaves those counters zero again, so one
- *                  workspace can serve any sequence of calls on a stream.
- *                  Calls that overlap in time must not share a workspace.
+ *                  aligned), or NULL when that size is 0; no initialization
+ *                  needed.  With act-order it receives x with its columns
+ *                  gathered through perm.  Calls that overlap in time must
+ *                  not share a workspace.
  * Accuracy: within max|y - ref| <= 1e-2 (1 + |ref|) elementwise and
  * relative Frobenius error <= 2e-3 of the float64 reference. */
 w4_status w4a16_linear(const w4_layer* layer, int64_t M, const void* x, const int32_t* tiled_qweight,

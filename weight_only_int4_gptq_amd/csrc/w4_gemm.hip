@@ -33,9 +33,11 @@
 //
 // Skinny kernel (the small-M, bandwidth-bound path): a workgroup owns NB
 // strips of 16 output columns and MT 16-row tiles of M; its KW waves split the
-// 128-row blocks of K between them (wave w takes blocks w, w + KW, ...), each
-// wave streaming 16 bytes per lane per block with one coalesced 1 KiB load,
-// and the KW partial results are summed in LDS at the end.
+// 128-row blocks of K into KW contiguous ranges, each wave streaming 16 bytes
+// per lane per block with one coalesced 1 KiB load, and the KW partial
+// results are summed in LDS at the end.  Each scale period (one group, at
+// most 128 rows) is accumulated exactly in fp32 from integer operands and
+// then added, times its fp32 scale, to the fp32 total.
 #include "w4_internal.h"
 
 namespace w4 {
@@ -200,14 +202,14 @@ __device__ __forceinline__ void block_mac(f4 (&tot)[MT][NB], const u4 (&a)[MT][4
 // rows to different banks.
 constexpr int kXPad = 8;
 
-// Registers of one run of U blocks: weights, scales and zeros of NB strips,
+// Registers of one 128-row block: weights, scales and zeros of NB strips,
 // and (unless the activations come from LDS) the A operands of MT row tiles.
-template <int U, int MT, int NB, int NP, bool XL>
-struct RunRegs {
-  u4 wv[U][NB];
-  uint16_t sraw[U][NB][NP];
-  uint32_t zraw[U][NB][NP];
-  u4 a[XL ? 1 : U][MT][4];
+template <int MT, int NB, int NP, bool XL>
+struct BlockRegs {
+  u4 wv[NB];
+  uint16_t sraw[NB][NP];
+  uint32_t zraw[NB][NP];
+  u4 a[XL ? 1 : MT][4];
 };
 
 // Per-lane view of the operands of one workgroup, with every pointer
@@ -287,61 +289,49 @@ struct LaneView {
     for (int j = 0; j < 4; ++j) a[0][j] = masked(row_ok[0], *reinterpret_cast<const u4*>(xl + kb * kTileK + 32 * j));
   }
 
-  // Weights, scales, zeros (and global A operands) of blocks kb .. kb+U-1 < hi.
-  template <int U>
-  __device__ __forceinline__ void load_run(int kb, int hi, RunRegs<U, MT, NB, NP, XL>& r) const {
+  // Weights, scales, zeros (and global A operands) of block b.
+  __device__ __forceinline__ void load_block(int b, BlockRegs<MT, NB, NP, XL>& r) const {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int b = kb + u;
-      if (b < hi) {  // wave-uniform
+    for (int s = 0; s < NB; ++s) {
+      r.wv[s] = w[s][(int64_t)b * 64];
 #pragma unroll
-      for (int s = 0; s < NB; ++s) {
-        r.wv[u][s] = w[s][(int64_t)b * 64];
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          const int g = Groups<GM>::group(b, p);
-          r.sraw[u][s][p] = sc[s][(int64_t)g * kTileN];
-          r.zraw[u][s][p] = HAS_Z ? zs[s][(int64_t)g * 2] : 0u;
-        }
-      }
-      if constexpr (!XL) load_a_global(b, r.a[u]);
+      for (int p = 0; p < NP; ++p) {
+        const int g = Groups<GM>::group(b, p);
+        r.sraw[s][p] = sc[s][(int64_t)g * kTileN];
+        r.zraw[s][p] = HAS_Z ? zs[s][(int64_t)g * 2] : 0u;
       }
     }
+    if constexpr (!XL) load_a_global(b, r.a);
   }
 };
 
 // Skinny kernel: see the header comment.  XL: activations staged in LDS.
-template <int MT, int NB, int KW, int U, int GM, bool BF16, bool HAS_Z, bool HAS_PERM, bool XL>
+template <int MT, int NB, int KW, int GM, bool BF16, bool HAS_Z, bool HAS_PERM, bool XL>
 __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restrict__ x, const u4* __restrict__ qw,
                                                         const uint16_t* __restrict__ sc,
                                                         const uint32_t* __restrict__ zs,
                                                         const int32_t* __restrict__ perm,
                                                         const uint16_t* __restrict__ bias,
                                                         uint16_t* __restrict__ y, int64_t M, int64_t K, int64_t N,
-                                                        int G, uint32_t* __restrict__ counters,
-                                                        float* __restrict__ partials) {
+                                                        int G) {
   static_assert(!XL || MT == 1, "LDS activations hold one 16-row tile");
   constexpr int NP = Groups<GM>::kPeriods;
   constexpr int R = MT * NB * 4;
   extern __shared__ float smem[];  // [KW][R][64] reduction buffer, then (XL) the activation rows
   float* red = smem;
   uint16_t* xlds = reinterpret_cast<uint16_t*>(smem + KW * R * 64);
-  __shared__ int last_arrival;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t t0 = (int64_t)blockIdx.x * NB;
   const int64_t m0 = (int64_t)blockIdx.y * 16 * MT;
-  const int KS = (int)gridDim.z, split = (int)blockIdx.z;
 
   LaneView<MT, NB, GM, HAS_Z, HAS_PERM, XL> v;
   v.init(x, qw, sc, zs, perm, xlds, t0, m0, M, K, G, lane);
   const int nblk = (int)v.nblk;
-  // split z of the workgroup grid owns blocks [z nblk / KS, (z + 1) nblk / KS);
-  // wave w owns the contiguous part [lo, hi) of it
-  const int64_t slo = ((int64_t)nblk * split) / KS, shi = ((int64_t)nblk * (split + 1)) / KS;
-  const int lo = __builtin_amdgcn_readfirstlane((int)(slo + ((shi - slo) * wave) / KW));
-  const int hi = __builtin_amdgcn_readfirstlane((int)(slo + ((shi - slo) * (wave + 1)) / KW));
+  // wave w owns the contiguous blocks [lo, hi) of K (wave-uniform bounds)
+  const int lo = __builtin_amdgcn_readfirstlane((int)(((int64_t)nblk * wave) / KW));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(((int64_t)nblk * (wave + 1)) / KW));
   const uint32_t zshift = 4u * (uint32_t)(lane & 7);
   const NibbleMasks nm = NibbleMasks::make();
 
@@ -351,14 +341,17 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
 #pragma unroll
     for (int s = 0; s < NB; ++s) tot[i][s] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // Runs of U blocks.  With LDS activations the runs are double buffered
-  // (the loads of run r + 1 are in flight while run r is computed) and the
-  // first run is issued before the staging so that its latency overlaps it;
-  // with register activations a single buffer keeps the register count, and
-  // so the occupancy, up (measured faster at M = 4..16).
-  RunRegs<U, MT, NB, NP, XL> ra, rb;
-  int kb = lo;
-  v.template load_run<U>(kb, hi, ra);
+  // Blocks are processed one at a time.  With LDS activations they are
+  // double buffered (the loads of block b + 1 are in flight while block b is
+  // computed) and the first block is issued before the staging so that its
+  // latency overlaps it; with register activations a single buffer keeps the
+  // register count, and so the occupancy, up (measured faster at M = 4..16).
+  // The steady-state loops contain no branch: the prefetch index is clamped
+  // to the wave's last block (one redundant in-bounds load at the end), so
+  // no branch join makes the compiler wait for every outstanding load.
+  const bool has_blocks = lo < hi;  // wave-uniform
+  BlockRegs<MT, NB, NP, XL> ra, rb;
+  if (has_blocks) v.load_block(lo, ra);
   if constexpr (XL) {
     const int64_t rows = (M - m0) < 16 ? (M - m0) : 16;
     const int64_t K8 = K / 8;
@@ -385,31 +378,31 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
     __syncthreads();
   }
 
-  auto compute = [&](int k0, RunRegs<U, MT, NB, NP, XL>& r) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (k0 + u < hi) {  // wave-uniform
-        if constexpr (XL) {
-          u4 a[MT][4];
-          v.load_a_lds(k0 + u, a);
-          block_mac<MT, NB, GM, BF16, HAS_Z>(tot, a, r.wv[u], r.sraw[u], r.zraw[u], zshift, nm);
-        } else {
-          block_mac<MT, NB, GM, BF16, HAS_Z>(tot, r.a[u], r.wv[u], r.sraw[u], r.zraw[u], zshift, nm);
-        }
-      }
+  auto compute = [&](int b, BlockRegs<MT, NB, NP, XL>& r) {
+    if constexpr (XL) {
+      u4 a[MT][4];
+      v.load_a_lds(b, a);
+      block_mac<MT, NB, GM, BF16, HAS_Z>(tot, a, r.wv, r.sraw, r.zraw, zshift, nm);
+    } else {
+      block_mac<MT, NB, GM, BF16, HAS_Z>(tot, r.a, r.wv, r.sraw, r.zraw, zshift, nm);
     }
   };
-  if constexpr (XL) {
-    for (; kb < hi; kb += 2 * U) {
-      v.template load_run<U>(kb + U, hi, rb);
-      compute(kb, ra);
-      v.template load_run<U>(kb + 2 * U, hi, ra);
-      compute(kb + U, rb);
-    }
-  } else {
-    for (; kb < hi; kb += U) {
-      compute(kb, ra);
-      v.template load_run<U>(kb + U, hi, ra);
+  if (has_blocks) {
+    const int last = hi - 1;
+    int kb = lo;
+    if constexpr (XL) {
+      for (; kb < last; kb += 2) {  // blocks kb and kb + 1 exist
+        v.load_block(kb + 1, rb);
+        compute(kb, ra);
+        v.load_block(kb + 2 < last ? kb + 2 : last, ra);
+        compute(kb + 1, rb);
+      }
+      if (kb == last) compute(kb, ra);  // odd count: ra holds the last block
+    } else {
+      for (; kb <= last; ++kb) {
+        compute(kb, ra);
+        v.load_block(kb + 1 < last ? kb + 1 : last, ra);
+      }
     }
   }
 
@@ -432,38 +425,6 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
       for (int w = 0; w < KW; ++w) acc[q] += red[w * R * 64 + e];
     }
   }
-  if (KS > 1) {
-    // Split-K fix-up.  Each workgroup stores its partial tile; the last of the
-    // KS workgroups of a tile to arrive sums the KS partials in split order
-    // (deterministic), finishes the tile and clears its counter for the next
-    // call.  No workgroup waits for another.
-    const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-    float* part = partials + tile * KS * (R * 64);
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int e = threadIdx.x + q * 64 * KW;
-      if (e < R * 64) part[(int64_t)split * (R * 64) + e] = acc[q];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      last_arrival = old == (uint32_t)(KS - 1);
-    }
-    __syncthreads();
-    if (!last_arrival) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int e = threadIdx.x + q * 64 * KW;
-      if (e < R * 64) {
-        float v = 0.f;
-        for (int z = 0; z < KS; ++z) v += part[(int64_t)z * (R * 64) + e];
-        acc[q] = v;
-      }
-    }
-    if (threadIdx.x == 0) __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     const int e = threadIdx.x + q * 64 * KW;
@@ -481,20 +442,20 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Wide kernel (the large-M, MFMA-bound path)
+// Wide kernel (M > 16: LDS-staged activations)
 //
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid over a 128 x 128 output
-// tile; wave (wm, wn) owns rows 64 wm .. 64 wm + 63 and strips 4 wn .. 4 wn + 3
-// of the tile (4 x 4 MFMA tiles of 16 x 16).  Per 128-row group of K:
-//   * the 128 x 128 activation tile is staged in LDS, double buffered, one
+// Workgroup: 256 threads = 4 waves in a 2 x 2 grid; wave (wm, wn) owns MT
+// 16-row tiles and NS strips, so the workgroup tile is 32 MT x 32 NS.  Per
+// 128-row group of K:
+//   * the 32 MT x 128 activation tile is staged in LDS, double buffered, one
 //     barrier per group, by direct global->LDS loads (no registers): 16-byte
 //     chunk j of row r is stored at chunk position j ^ (r % 16) of the row,
 //     so the 16 rows that one A-operand read touches fall on distinct banks;
-//   * each wave streams the packed words of its 4 strips straight from HBM
+//   * each wave streams the packed words of its NS strips straight from HBM
 //     into registers (one 16-byte load per strip per lane), prefetched one
 //     group ahead together with scales and zeros;
-//   * for each K step the four strips are dequantized in registers and fed
-//     to 16 MFMAs.
+//   * for each K step the NS strips are dequantized in registers and fed to
+//     MT x NS MFMAs.
 // Scaling uses one accumulator set per tile: at the start of scale period g
 // the fp32 accumulator (which holds sum_{h<g} P_h s_h / s_{g-1}) is
 // multiplied by s_{g-1} / s_g, the MFMAs then add the exact integer-weighted
@@ -502,14 +463,15 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
 // the end.  The tile layout never stores a zero scale (the repack replaces
 // it and zeroes the codes' contribution), so every ratio is finite; each
 // multiply adds one fp32 rounding (relative 2^-24 per period).
-// Rows >= M are staged as zeros and never stored; strips >= N/16 are skipped.
+// Rows >= M are staged from row M - 1 and never stored; strips >= N/16 are
+// skipped.  MT = 4, NS = 4 (128 x 128) serves prefill; smaller tiles give
+// mid-size M enough workgroups.
 // ---------------------------------------------------------------------------
-constexpr int kWideBM = 128, kWideBN = 128, kWideThreads = 256;
-constexpr int kWideLdsStride = kTileK;  // halves per staged activation row (swizzled, unpadded)
+constexpr int kWideThreads = 256;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int GM, bool BF16, bool HAS_Z>
+template <int MT, int NS, int GM, bool BF16, bool HAS_Z>
 __global__ __launch_bounds__(kWideThreads, 2) void gemm_wide(const uint16_t* __restrict__ x,
                                                                const u4* __restrict__ qw,
                                                                const uint16_t* __restrict__ sc,
@@ -518,7 +480,10 @@ __global__ __launch_bounds__(kWideThreads, 2) void gemm_wide(const uint16_t* __r
                                                                uint16_t* __restrict__ y, int64_t M, int64_t K,
                                                                int64_t N, int G) {
   constexpr int NP = Groups<GM>::kPeriods, SP = Groups<GM>::kSteps;
-  __shared__ __attribute__((aligned(1024))) uint16_t xs[2][kWideBM * kWideLdsStride];
+  constexpr int BM = 32 * MT;           // rows per workgroup tile
+  constexpr int STRIPS = 2 * NS;        // strips per workgroup tile
+  constexpr int kStage = BM / 16;       // staging loads per wave per group (4 rows each)
+  __shared__ __attribute__((aligned(1024))) uint16_t xs[2][BM * kTileK];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -526,55 +491,57 @@ __global__ __launch_bounds__(kWideThreads, 2) void gemm_wide(const uint16_t* __r
   const int c = lane & 15, quad = lane >> 4;
   const int64_t T = N / kTileN;
   const int64_t nblk = K / kTileK;
-  const int64_t m0 = (int64_t)blockIdx.y * kWideBM;
-  const int64_t tw0 = (int64_t)blockIdx.x * (kWideBN / kTileN) + 4 * wn;  // first strip of this wave
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const int64_t tw0 = (int64_t)blockIdx.x * STRIPS + NS * wn;  // first strip of this wave
   const uint32_t zshift = 4u * (uint32_t)(c & 7);
   const NibbleMasks nm = NibbleMasks::make();
 
-  // staging: instruction i of wave w fills rows 32 w + 4 i .. + 3 of the
-  // tile; lane l lands at chunk position l % 16 of row 32 w + 4 i + l / 16
-  // and so loads logical chunk (l % 16) ^ (row % 16).  Rows >= M load row
-  // M - 1: their outputs are never stored.
+  // staging: instruction i of wave w fills rows (kStage w + i) * 4 .. + 3 of
+  // the tile; lane l lands at chunk position l % 16 of row base + l / 16 and
+  // so loads logical chunk (l % 16) ^ (row % 16).
   auto stage = [&](int64_t kb, int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 32 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < kStage; ++i) {
+      const int row0 = 4 * (kStage * wave + i);
+      const int row = row0 + (lane >> 4);
       int64_t m = m0 + row;
       m = m < M ? m : M - 1;
       const int j = (lane & 15) ^ (row & 15);
       const uint16_t* src = x + m * K + kb * kTileK + 8 * j;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)&xs[buf][(32 * wave + 4 * i) * kWideLdsStride], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)&xs[buf][row0 * kTileK], 16, 0, 0);
     }
   };
+
   struct Meta {
-    u4 w[4];
-    uint16_t s[4][NP];
-    uint32_t z[4][NP];
+    u4 w[NS];
+    uint16_t s[NS][NP];
+    uint32_t z[NS][NP];
   };
   auto load_meta = [&](int64_t kb, Meta& mt) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < NS; ++nt) {
       const int64_t t = tw0 + nt;
-      const bool ok = t < T;
+      const bool ok = t < T;  // wave-uniform
       const int64_t tt = ok ? t : 0;
-      mt.w[nt] = u4{0u, 0u, 0u, 0u};
-      if (ok) mt.w[nt] = qw[(tt * nblk + kb) * 64 + lane];
+      mt.w[nt] = qw[(tt * nblk + kb) * 64 + lane];
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int64_t g = Groups<GM>::group((int)kb, p);
-        mt.s[nt][p] = ok ? sc[(tt * G + g) * kTileN + c] : (uint16_t)0;
-        mt.z[nt][p] = (HAS_Z && ok) ? zs[(tt * G + g) * 2 + (c >> 3)] : 0u;
+        mt.s[nt][p] = sc[(tt * G + g) * kTileN + c];
+        mt.z[nt][p] = HAS_Z ? zs[(tt * G + g) * 2 + (c >> 3)] : 0u;
       }
     }
   };
 
-  f4 acc[4][4];
+  f4 acc[MT][NS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NS; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
   const u4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  float s_prev[4] = {1.f, 1.f, 1.f, 1.f};
+  float s_prev[NS];
+#pragma unroll
+  for (int nt = 0; nt < NS; ++nt) s_prev[nt] = 1.f;
 
   Meta cur, nxt;
   stage(0, 0);
@@ -583,19 +550,18 @@ __global__ __launch_bounds__(kWideThreads, 2) void gemm_wide(const uint16_t* __r
   for (int64_t kb = 0; kb < nblk; ++kb) {
     const int buf = (int)(kb & 1);
     __syncthreads();  // tile kb visible; buffer buf ^ 1 free
-    const bool more = kb + 1 < nblk;
-    if (more) {
-      stage(kb + 1, buf ^ 1);
-      load_meta(kb + 1, nxt);
-    }
-    // row of this lane in tile i: 64 wm + 16 i + c, so row % 16 == c
-    const uint16_t* xa = &xs[buf][(64 * wm + c) * kWideLdsStride];
+    // prefetch (clamped at the last group: one redundant in-bounds load)
+    const int64_t kn = kb + 1 < nblk ? kb + 1 : kb;
+    stage(kn, buf ^ 1);
+    load_meta(kn, nxt);
+    // row of this lane in tile i: 16 (MT wm + i) + c, so row % 16 == c
+    const uint16_t* xa = &xs[buf][(16 * MT * wm + c) * kTileK];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      uint32_t n1[4], n2[4];
-      float nzz[4];
+      uint32_t n1[NS], n2[NS];
+      float nzz[NS];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NS; ++nt) {
         const uint32_t z = HAS_Z ? (cur.z[nt][p] >> zshift) & 0xFu : 8u;
         n1[nt] = nz1024_bits(z);
         n2[nt] = nz64_bits(z);
@@ -604,72 +570,64 @@ __global__ __launch_bounds__(kWideThreads, 2) void gemm_wide(const uint16_t* __r
         if constexpr (GM != GM_CH) {
           const float r = s_prev[nt] * __builtin_amdgcn_rcpf(s_cur);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[i][nt][q] *= r;
         }
         s_prev[nt] = s_cur;
       }
-      f4 rs[4];
+      f4 rs[MT];
       if constexpr (BF16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rs[i] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < MT; ++i) rs[i] = f4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int j = p * SP; j < (p + 1) * SP; ++j) {
-        u4 a[4];
+        u4 a[MT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a[i] = *reinterpret_cast<const u4*>(xa + 16 * i * kWideLdsStride + 8 * ((4 * j + quad) ^ c));
+        for (int i = 0; i < MT; ++i) a[i] = *reinterpret_cast<const u4*>(xa + 16 * i * kTileK + 8 * ((4 * j + quad) ^ c));
         if constexpr (BF16) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) rs[i] = mfma<true>(a[i], ones, rs[i]);
+          for (int i = 0; i < MT; ++i) rs[i] = mfma<true>(a[i], ones, rs[i]);
         }
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < NS; ++nt) {
           u4 b;
           if constexpr (BF16)
             b = dq_bf16(cur.w[nt][j], nm);
           else
             b = dq_f16(cur.w[nt][j], n1[nt], n2[nt], nm);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i][nt] = mfma<BF16>(a[i], b, acc[i][nt]);
+          for (int i = 0; i < MT; ++i) acc[i][nt] = mfma<BF16>(a[i], b, acc[i][nt]);
         }
       }
       if constexpr (BF16) {
         // remove (128 + z) * sum_k x[m, k] of this period
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < NS; ++nt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[i][nt][q] = __builtin_fmaf(nzz[nt], rs[i][q], acc[i][nt][q]);
       }
     }
-    if (more) cur = nxt;
-    __builtin_amdgcn_s_waitcnt(0);  // tile kb + 1 has landed before the barrier publishes it
+    cur = nxt;
+    __builtin_amdgcn_s_waitcnt(0);  // the next tile has landed before the barrier publishes it
   }
-  f4 tot[4][4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) tot[i][nt][q] = acc[i][nt][q] * s_prev[nt];
 
   // epilogue: lane holds column c of each strip, rows 4 quad + r of each tile
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < NS; ++nt) {
     const int64_t t = tw0 + nt;
     if (t >= T) continue;
     const int64_t n = t * kTileN + c;
     const float b = bias != nullptr ? act_to_f32<BF16>(bias[n]) : 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + 64 * wm + 16 * i + 4 * quad + r;
-        if (m < M) y[m * N + n] = f32_to_act<BF16>(tot[i][nt][r] + b);
+        const int64_t m = m0 + 16 * (MT * wm + i) + 4 * quad + r;
+        if (m < M) y[m * N + n] = f32_to_act<BF16>(acc[i][nt][r] * s_prev[nt] + b);
       }
   }
 }
@@ -697,9 +655,6 @@ struct Args {
   uint16_t* y;
   int64_t M, K, N;
   int G, gs;
-  int ks;               // workgroups splitting K (gridDim.z)
-  uint32_t* counters;   // split-K arrival counters (zero between calls)
-  float* partials;      // split-K partial tiles
 };
 
 // LDS bytes of a skinny launch: the reduction buffer, plus the staged
@@ -712,12 +667,12 @@ inline size_t skinny_lds_bytes(int mt, int nb, int kw, bool xl, int64_t M, int64
   return b;
 }
 
-template <int MT, int NB, int KW, int U, int GM, bool BF16, bool HZ, bool HP, bool XL>
+template <int MT, int NB, int KW, int GM, bool BF16, bool HZ, bool HP, bool XL>
 hipError_t run_skinny(const Args& a, hipStream_t st) {
-  const dim3 grid((unsigned)(a.N / (kTileN * NB)), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)), (unsigned)a.ks);
+  const dim3 grid((unsigned)(a.N / (kTileN * NB)), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
   const size_t lds = skinny_lds_bytes(MT, NB, KW, XL, a.M, a.K);
-  gemm_skinny<MT, NB, KW, U, GM, BF16, HZ, HP, XL><<<grid, 64 * KW, lds, st>>>(
-      a.x, a.qw, a.sc, a.zs, a.perm, a.bias, a.y, a.M, a.K, a.N, a.G, a.counters, a.partials);
+  gemm_skinny<MT, NB, KW, GM, BF16, HZ, HP, XL><<<grid, 64 * KW, lds, st>>>(
+      a.x, a.qw, a.sc, a.zs, a.perm, a.bias, a.y, a.M, a.K, a.N, a.G);
   return hipGetLastError();
 }
 
@@ -728,111 +683,120 @@ inline int group_mode(int gs, int64_t K) {
   return GM_CH;  // per-channel: one group of K rows
 }
 
-template <int GM, bool BF16, bool HZ>
-hipError_t run_wide(const Args& a, const uint16_t* x, hipStream_t st) {
-  const dim3 grid((unsigned)((a.N / kTileN + (kWideBN / kTileN) - 1) / (kWideBN / kTileN)),
-                  (unsigned)((a.M + kWideBM - 1) / kWideBM));
-  gemm_wide<GM, BF16, HZ><<<grid, kWideThreads, 0, st>>>(x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N, a.G);
+hipError_t launch_gather(const uint16_t* x, const int32_t* perm, uint16_t* xp, int64_t M, int64_t K, hipStream_t st) {
+  const int64_t total = M * K;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  gather_columns<<<(unsigned)blocks, 256, 0, st>>>(x, perm, xp, M, K);
   return hipGetLastError();
 }
 
-template <bool BF16, bool HZ>
+template <int MT, int NS, int GM, bool BF16, bool HZ>
+hipError_t run_wide(const Args& a, const uint16_t* x, hipStream_t st) {
+  const int64_t T = a.N / kTileN;
+  const dim3 grid((unsigned)((T + 2 * NS - 1) / (2 * NS)), (unsigned)((a.M + 32 * MT - 1) / (32 * MT)));
+  gemm_wide<MT, NS, GM, BF16, HZ><<<grid, kWideThreads, 0, st>>>(x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N,
+                                                                   a.G);
+  return hipGetLastError();
+}
+
+template <int MT, int NS, bool BF16, bool HZ>
 hipError_t wide_gm(const Args& a, const uint16_t* x, hipStream_t st) {
   switch (group_mode(a.gs, a.K)) {
-    case GM_32: return run_wide<GM_32, BF16, HZ>(a, x, st);
-    case GM_64: return run_wide<GM_64, BF16, HZ>(a, x, st);
-    case GM_128: return run_wide<GM_128, BF16, HZ>(a, x, st);
-    default: return run_wide<GM_CH, BF16, HZ>(a, x, st);
+    case GM_32: return run_wide<MT, NS, GM_32, BF16, HZ>(a, x, st);
+    case GM_64: return run_wide<MT, NS, GM_64, BF16, HZ>(a, x, st);
+    case GM_128: return run_wide<MT, NS, GM_128, BF16, HZ>(a, x, st);
+    default: return run_wide<MT, NS, GM_CH, BF16, HZ>(a, x, st);
   }
+}
+
+template <int MT, int NS>
+hipError_t wide_flags(const Shape& s, const Args& a, const uint16_t* x, hipStream_t st) {
+  if (s.bf16) return s.has_z ? wide_gm<MT, NS, true, true>(a, x, st) : wide_gm<MT, NS, true, false>(a, x, st);
+  return s.has_z ? wide_gm<MT, NS, false, true>(a, x, st) : wide_gm<MT, NS, false, false>(a, x, st);
 }
 
 // Act-order first gathers the columns of x into the workspace.
-hipError_t launch_wide(const Shape& s, const Args& a, void* ws, hipStream_t st) {
+hipError_t launch_wide(const Shape& s, const GemmPlan& p, const Args& a, void* ws, hipStream_t st) {
   const uint16_t* x = a.x;
   if (s.has_perm) {
     uint16_t* xp = static_cast<uint16_t*>(ws);
-    const int64_t total = a.M * a.K;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    gather_columns<<<(unsigned)blocks, 256, 0, st>>>(a.x, a.perm, xp, a.M, a.K);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_gather(a.x, a.perm, xp, a.M, a.K, st);
     if (e != hipSuccess) return e;
     x = xp;
   }
-  if (s.bf16) return s.has_z ? wide_gm<true, true>(a, x, st) : wide_gm<true, false>(a, x, st);
-  return s.has_z ? wide_gm<false, true>(a, x, st) : wide_gm<false, false>(a, x, st);
+  if (p.mt == 4) return p.nb == 4 ? wide_flags<4, 4>(s, a, x, st) : p.nb == 2 ? wide_flags<4, 2>(s, a, x, st)
+                                                                              : wide_flags<4, 1>(s, a, x, st);
+  if (p.mt == 2) return p.nb == 2 ? wide_flags<2, 2>(s, a, x, st) : wide_flags<2, 1>(s, a, x, st);
+  return p.nb == 2 ? wide_flags<1, 2>(s, a, x, st) : wide_flags<1, 1>(s, a, x, st);
 }
 
-template <int MT, int NB, int KW, int U, bool XL, bool BF16, bool HZ, bool HP>
+template <int MT, int NB, int KW, bool XL, bool BF16, bool HZ, bool HP>
 hipError_t pick_gm(const Args& a, hipStream_t st) {
   switch (group_mode(a.gs, a.K)) {
-    case GM_32: return run_skinny<MT, NB, KW, U, GM_32, BF16, HZ, HP, XL>(a, st);
-    case GM_64: return run_skinny<MT, NB, KW, U, GM_64, BF16, HZ, HP, XL>(a, st);
-    case GM_128: return run_skinny<MT, NB, KW, U, GM_128, BF16, HZ, HP, XL>(a, st);
-    default: return run_skinny<MT, NB, KW, U, GM_CH, BF16, HZ, HP, XL>(a, st);
+    case GM_32: return run_skinny<MT, NB, KW, GM_32, BF16, HZ, HP, XL>(a, st);
+    case GM_64: return run_skinny<MT, NB, KW, GM_64, BF16, HZ, HP, XL>(a, st);
+    case GM_128: return run_skinny<MT, NB, KW, GM_128, BF16, HZ, HP, XL>(a, st);
+    default: return run_skinny<MT, NB, KW, GM_CH, BF16, HZ, HP, XL>(a, st);
   }
 }
 
-template <int MT, int NB, int KW, int U, bool XL>
+template <int MT, int NB, int KW, bool XL>
 hipError_t pick_flags(const Shape& s, const Args& a, hipStream_t st) {
+  // act-order reaches the kernels only on the LDS-staged path (which gathers
+  // while staging); the register path receives pre-gathered activations
+  const bool hp = XL && s.has_perm;
   if (s.bf16) {
     if (s.has_z)
-      return s.has_perm ? pick_gm<MT, NB, KW, U, XL, true, true, true>(a, st)
-                        : pick_gm<MT, NB, KW, U, XL, true, true, false>(a, st);
-    return s.has_perm ? pick_gm<MT, NB, KW, U, XL, true, false, true>(a, st)
-                      : pick_gm<MT, NB, KW, U, XL, true, false, false>(a, st);
+      return hp ? pick_gm<MT, NB, KW, XL, true, true, XL>(a, st) : pick_gm<MT, NB, KW, XL, true, true, false>(a, st);
+    return hp ? pick_gm<MT, NB, KW, XL, true, false, XL>(a, st) : pick_gm<MT, NB, KW, XL, true, false, false>(a, st);
   }
   if (s.has_z)
-    return s.has_perm ? pick_gm<MT, NB, KW, U, XL, false, true, true>(a, st)
-                      : pick_gm<MT, NB, KW, U, XL, false, true, false>(a, st);
-  return s.has_perm ? pick_gm<MT, NB, KW, U, XL, false, false, true>(a, st)
-                    : pick_gm<MT, NB, KW, U, XL, false, false, false>(a, st);
+    return hp ? pick_gm<MT, NB, KW, XL, false, true, XL>(a, st) : pick_gm<MT, NB, KW, XL, false, true, false>(a, st);
+  return hp ? pick_gm<MT, NB, KW, XL, false, false, XL>(a, st) : pick_gm<MT, NB, KW, XL, false, false, false>(a, st);
 }
 
 }  // namespace
 
 GemmPlan plan_gemm(const Shape& s, int64_t M) {
-  // (mt, nb, kw, u, ks, xl): 16-row tiles per wave, strips per workgroup,
-  // waves per workgroup (splitting K), blocks per load run, workgroups
-  // splitting K, activations staged in LDS.  Chosen from timing sweeps of
-  // the decode shapes on MI355X.
+  // (mt, nb, kw, xl): 16-row tiles per wave, strips per workgroup, waves per
+  // workgroup (splitting K), activations staged in LDS.  Chosen from timing
+  // sweeps of the decode shapes on MI355X.  K is never split across
+  // workgroups: the agent-scope release fence that a cross-workgroup fix-up
+  // needs writes back the XCD's whole L2 on gfx950 and cost far more than it
+  // saved at these sizes (measured).
   GemmPlan p;
   const bool deep_k = s.K >= 8192 || s.N <= 4096;  // few strips: more waves per strip
-  if (M == 1 && skinny_lds_bytes(1, 1, 16, true, M, s.K) <= kMaxSkinnyLds) {
-    p = deep_k ? GemmPlan{GemmKind::kSkinny, 1, 1, 16, 1, 1, true, "w4_skinny_m1_lds_k16"}
-               : GemmPlan{GemmKind::kSkinny, 1, 1, 8, 1, 1, true, "w4_skinny_m1_lds_k8"};
+  const int64_t T = s.N / kTileN;
+  if (M <= 4 && skinny_lds_bytes(1, 1, 8, true, M, s.K) <= kMaxSkinnyLds) {
+    const bool k16 = deep_k && skinny_lds_bytes(1, 1, 16, true, M, s.K) <= kMaxSkinnyLds;
+    p = k16 ? GemmPlan{GemmKind::kSkinny, 1, 1, 16, true, "w4_skinny_lds_k16"}
+            : GemmPlan{GemmKind::kSkinny, 1, 1, 8, true, "w4_skinny_lds_k8"};
   } else if (M <= 16) {
-    if (s.N >= 12288) p = GemmPlan{GemmKind::kSkinny, 1, 2, 16, 1, 1, false, "w4_skinny_m16_n2_k16"};
-    else if (M <= 4) p = GemmPlan{GemmKind::kSkinny, 1, 1, 16, 1, 1, false, "w4_skinny_m16_k16"};
-    else p = GemmPlan{GemmKind::kSkinny, 1, 1, 8, 1, 1, false, "w4_skinny_m16_k8"};
-  } else if (M <= 32) {
-    p = GemmPlan{GemmKind::kSkinny, 2, 1, 8, 1, 1, false, "w4_skinny_m32"};
-  } else if (M <= 64) {
-    p = GemmPlan{GemmKind::kSkinny, 4, 1, 4, 1, 1, false, "w4_skinny_m64"};
+    if (s.N >= 12288 && T % 4 == 0) p = GemmPlan{GemmKind::kSkinny, 1, 4, 16, false, "w4_skinny_n4_k16"};
+    else if (M <= 4 || s.K >= 8192) p = GemmPlan{GemmKind::kSkinny, 1, 1, 16, false, "w4_skinny_k16"};
+    else p = GemmPlan{GemmKind::kSkinny, 1, 1, 8, false, "w4_skinny_k8"};
   } else {
-    p = GemmPlan{GemmKind::kWide, 0, 0, 0, 0, 1, false, s.has_perm ? "w4_wide_128x128_gather" : "w4_wide_128x128"};
+    // wide kernel: wave tile mt x 16 rows by nb strips; the largest tile that
+    // still gives >= 512 workgroups (2 per CU), else the smallest
+    const int mt = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
+    const int64_t mtiles = (M + 32 * mt - 1) / (32 * mt);
+    int nb = mt == 4 ? 4 : 2;
+    while (nb > 1 && ((T + 2 * nb - 1) / (2 * nb)) * mtiles < 512) nb /= 2;
+    static const char* names[5][5] = {{}, {"", "w4_wide_32x32", "w4_wide_32x64"},
+                                      {"", "w4_wide_64x32", "w4_wide_64x64"}, {},
+                                      {"", "w4_wide_128x32", "w4_wide_128x64", "", "w4_wide_128x128"}};
+    p = GemmPlan{GemmKind::kWide, mt, nb, 4, false, names[mt][nb]};
   }
-  // No split of K across workgroups: the agent-scope release fence that the
-  // split-K fix-up needs writes back the XCD's whole L2 on gfx950 and costs
-  // far more than it saves at these sizes (measured).
-  p.ks = 1;
   return p;
 }
 
-namespace {
-int64_t tiles_of(const Shape& s, int64_t M, const GemmPlan& p) {
-  return (s.N / (kTileN * p.nb)) * ((M + 16 * p.mt - 1) / (16 * p.mt));
-}
-constexpr size_t kCounterAlign = 256;
-}  // namespace
-
 size_t gemm_workspace_bytes(const Shape& s, int64_t M) {
   const GemmPlan p = plan_gemm(s, M);
-  if (p.kind == GemmKind::kWide) return s.has_perm ? (size_t)M * (size_t)s.K * sizeof(uint16_t) : 0;
-  if (p.ks <= 1) return 0;
-  const size_t tiles = (size_t)tiles_of(s, M, p);
-  const size_t counters = (tiles * sizeof(uint32_t) + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
-  return counters + tiles * p.ks * (size_t)(p.mt * p.nb * 4 * 64) * sizeof(float);
+  // act-order: every path except the LDS-staged skinny kernel gathers the
+  // columns of x into the workspace first
+  if (s.has_perm && !p.xl) return (size_t)M * (size_t)s.K * sizeof(uint16_t);
+  return 0;
 }
 
 hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* tiled_w, const void* tiled_s,
@@ -852,21 +816,21 @@ hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* 
   a.G = s.G;
   a.gs = s.gs;
   const GemmPlan p = plan_gemm(s, M);
-  a.ks = p.ks;
-  a.counters = nullptr;
-  a.partials = nullptr;
-  if (p.ks > 1) {
-    const size_t tiles = (size_t)tiles_of(s, M, p);
-    const size_t counters = (tiles * sizeof(uint32_t) + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
-    a.counters = static_cast<uint32_t*>(ws);
-    a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + counters);
+  if (p.kind == GemmKind::kWide) return launch_wide(s, p, a, ws, st);
+  Shape sk = s;
+  if (s.has_perm && !p.xl) {
+    // gather x[:, perm] into the workspace, then run without act-order
+    uint16_t* xp = static_cast<uint16_t*>(ws);
+    const hipError_t e = launch_gather(a.x, a.perm, xp, a.M, a.K, st);
+    if (e != hipSuccess) return e;
+    a.x = xp;
+    a.perm = nullptr;
+    sk.has_perm = false;
   }
-  if (p.kind == GemmKind::kWide) return launch_wide(s, a, ws, st);
-  if (p.xl) return p.kw == 16 ? pick_flags<1, 1, 16, 1, true>(s, a, st) : pick_flags<1, 1, 8, 1, true>(s, a, st);
-  if (p.mt == 1 && p.nb == 2) return pick_flags<1, 2, 16, 1, false>(s, a, st);
-  if (p.mt == 1) return p.kw == 16 ? pick_flags<1, 1, 16, 1, false>(s, a, st) : pick_flags<1, 1, 8, 1, false>(s, a, st);
-  if (p.mt == 2) return pick_flags<2, 1, 8, 1, false>(s, a, st);
-  return pick_flags<4, 1, 4, 1, false>(s, a, st);
+  if (p.xl) return p.kw == 16 ? pick_flags<1, 1, 16, true>(sk, a, st) : pick_flags<1, 1, 8, true>(sk, a, st);
+  if (p.mt == 1 && p.nb == 4) return pick_flags<1, 4, 16, false>(sk, a, st);
+  if (p.mt == 1) return p.kw == 16 ? pick_flags<1, 1, 16, false>(sk, a, st) : pick_flags<1, 1, 8, false>(sk, a, st);
+  return pick_flags<1, 1, 8, false>(sk, a, st);
 }
 
 }  // namespace w4

@@ -53,8 +53,6 @@ struct GemmPlan {
   int mt;        // 16-row M tiles per wave (skinny kernel)
   int nb;        // strips per workgroup
   int kw;        // waves splitting K inside a workgroup
-  int u;         // 128-row blocks per load run
-  int ks;        // workgroups splitting K (split-K fix-up through the workspace)
   bool xl;       // activations staged in LDS
   const char* name;
 };

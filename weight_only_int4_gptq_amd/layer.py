@@ -102,11 +102,10 @@ class W4A16Linear:
         return y.reshape(*lead, self.N)
 
     def _workspace(self, nbytes: int, device) -> "torch.Tensor":
-        """A zero-filled scratch buffer of at least nbytes, kept for later
-        calls (the library leaves its split-K counters zero after each call)."""
+        """A scratch buffer of at least nbytes, kept for later calls."""
         ws = getattr(self, "_ws", None)
         if ws is None or ws.numel() < nbytes or ws.device != torch.device(device):
-            ws = torch.zeros((nbytes,), dtype=torch.uint8, device=device)
+            ws = torch.empty((nbytes,), dtype=torch.uint8, device=device)
             self._ws = ws
         return ws
 
