@@ -34,6 +34,7 @@ METRIC = "W4A16 GEMM TFLOPS + packed-weight HBM GB/s (% roofline), M=1..8192"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
 ROTATE_BYTES = 512 << 20       # working set per shape, > 256 MB MALL
+COPY_PROBE_BYTES = 256 << 20   # plain device copy used to calibrate byte counters
 
 
 def parse():
@@ -46,6 +47,25 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     return p.parse_args()
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "skinny_decode_hbm_traffic.txt")
+GEMM_SOURCE = os.path.join(ROOT, "weight_only_int4_gptq_amd", "csrc", "w4_gemm.hip")
+
+
+def measured_traffic():
+    """HBM bytes per decode GEMM launch from the committed rocprofv3 counter
+    summary, or None when the GEMM source changed since it was measured."""
+    import hashlib
+    try:
+        fields = dict(line.split(": ", 1) for line in open(TRAFFIC_PROFILE).read().splitlines()
+                      if line and not line.startswith("#") and ": " in line)
+        cur = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if fields.get("source_sha256", "").strip() != cur:
+        return None
+    return int(float(fields["per_launch_traffic_bytes"]))
 
 
 def _to_dev(torch, a):
@@ -159,6 +179,15 @@ def main():
                              pct_mfma=round(100 * flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 1),
                              _wb=wb, _tb=tb, _flops=flops, _us=us))
 
+    # ---- copy of known size (not timed): the reference for the HBM byte
+    # counters when this run is profiled (FETCH_SIZE / WRITE_SIZE) ----
+    src = torch.empty((COPY_PROBE_BYTES,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
     # ---- the timed steps ----
     for _ in range(args.warmup):
         step()
@@ -190,6 +219,8 @@ def main():
         ach = sum_fl / (sum_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+    if hbm_bound and args.config == "decode":
+        roof["traffic"] = measured_traffic()
     roof["kernel"] = sorted({p["kernel"] for p in per_case})
     roof["per_launch_bytes_avg"] = round(sum_tb / len(per_case))
     roof["avg_launch_us"] = round(sum_us / len(per_case), 3)
@@ -218,6 +249,7 @@ def main():
                         + f" x M in {list(c0.Ms)}; {c0.fmt.upper()} g={c0.group_size}"
                         + (" zeros" if c0.has_zeros else " symmetric") + (" act-order" if c0.has_gidx else ""),
             "cases": len(runs), "act_dtype": c0.dtype, "weight_rotation_MiB": ROTATE_BYTES >> 20,
+            "copy_probe_MiB": COPY_PROBE_BYTES >> 20,
         },
         "tflops_step": round(flops_step / (ms_step * 1e-3) / 1e12, 3),
         "wall_s_timed": round(wall, 3),
