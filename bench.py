@@ -5,7 +5,10 @@
 A step is one forward pass of the hot path over every (shape, M) case of the
 chosen workload: for each case one w4a16_linear call (host validation, kernel
 selection, fused dequantize + GEMM, epilogue) on activations and weights that
-are already resident in HBM.  The one-time repacks (AWQ -> standard ->
+are already resident in HBM.  The timed launches are recorded into a HIP
+graph and replayed (as a serving loop would), so the ~5 us host cost of a
+Python call does not starve the GPU between short decode kernels; --eager
+times direct launches instead.  The one-time repacks (AWQ -> standard ->
 tile layout) are timed separately and reported under "repack".
 
 Weight buffers are rotated over enough copies that every launch reads its
@@ -46,6 +49,8 @@ def parse():
     p.add_argument("--reps", type=int, default=0, help="launches per case for the per-kernel timing (0 = auto)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--eager", action="store_true",
+                   help="time direct launches instead of HIP-graph replays (host launch cost included)")
     return p.parse_args()
 
 
@@ -145,14 +150,41 @@ def main():
                              kernel=lyr.kernel_name(M)))
 
     def launch(r):
+        # the current stream: the capture stream while a HIP graph is recorded
         t = r["sets"][r["i"] % len(r["sets"])]
         r["i"] += 1
         W.w4a16_linear(r["lyr"].layer, r["M"], r["x"], t["qweight"], t["scales"], t["qzeros"], t["perm"], None,
-                       r["y"], r["ws"] if r["ws_b"] else None, r["ws_b"], stream)
+                       r["y"], r["ws"] if r["ws_b"] else None, r["ws_b"], torch.cuda.current_stream())
 
     def step():
         for r in runs:
             launch(r)
+
+    def timed(fn, count):
+        """Milliseconds for the launches that fn() enqueues, HIP events on the
+        launch stream.  By default fn's launches are recorded once into a HIP
+        graph, which is replayed once untimed (upload) and once timed, so the
+        host's per-call cost (Python, ctypes, validation: ~5 us) does not
+        starve the GPU between short kernels, as in a serving loop."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.eager:
+            torch.cuda.synchronize()
+            e0.record(stream)
+            fn(count)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(count)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1)
 
     # ---- per-kernel timing: HIP events on the launch stream ----
     per_case = []
@@ -162,13 +194,7 @@ def main():
         for _ in range(5):
             launch(r)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            launch(r)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+        us = timed(lambda n: [launch(r) for _ in range(n)], reps) * 1e3 / reps
         wb, tb = case_bytes(c, M)
         flops = 2.0 * M * c.K * c.N
         per_case.append(dict(K=c.K, N=c.N, M=M, kernel=r["kernel"], us=round(us, 3),
@@ -192,15 +218,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
+    ms_step = timed(lambda n: [step() for _ in range(n)], args.steps) / args.steps
     wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / args.steps
 
     wbytes_step = sum(case_bytes(r["c"], r["M"])[0] for r in runs)
     flops_step = sum(2.0 * r["M"] * r["c"].K * r["c"].N for r in runs)
@@ -251,6 +271,8 @@ def main():
             "cases": len(runs), "act_dtype": c0.dtype, "weight_rotation_MiB": ROTATE_BYTES >> 20,
             "copy_probe_MiB": COPY_PROBE_BYTES >> 20,
         },
+        "timing": ("eager launches" if args.eager else
+                   "HIP graph of the timed launches (one untimed replay uploads it, one replay is timed)"),
         "tflops_step": round(flops_step / (ms_step * 1e-3) / 1e12, 3),
         "wall_s_timed": round(wall, 3),
         "roofline": roof,

@@ -366,3 +366,88 @@ def test_linear_full_size_sampled(W, c, M):
     ref = O.reference_entries(x, c.fmt, c.dtype, Lw["qweight"], Lw["qzeros"], Lw["scales"], c.group_size, rows,
                               cols, g_idx=Lw["g_idx"])
     _assert_close(y[rows, cols], ref, c.dtype, f"{c.label} M={M} (sampled {ns})")
+
+
+# ----------------------------------------------------------------------------
+# GEMM: every wide-kernel tile configuration, every group mode and dtype
+# ----------------------------------------------------------------------------
+
+# (M, N) pairs that select each wide tile of the kernel table (64x256 with a
+# 4- and a 3-deep pipeline, 64x128, 32x128, 32x64); K = 1152 is nine 128-row
+# blocks, so every pipeline depth runs full trips and a partial tail.
+WIDE_TILE_SHAPES = [(1024, 16384), (256, 16384), (64, 32768), (32, 32768), (40, 8192)]
+WIDE_VARIANTS = [
+    # (name, fmt, group_size, has_zeros, has_gidx, dtype)
+    ("awq-fp16-g128", "awq", 128, True, False, "fp16"),
+    ("std-bf16-g128-sym", "std", 128, False, False, "bf16"),
+    ("std-fp16-g32-z", "std", 32, True, False, "fp16"),
+    ("std-bf16-g64-z", "std", 64, True, False, "bf16"),
+    ("std-fp16-ch-z", "std", -1, True, False, "fp16"),
+    ("std-fp16-g128-z-act", "std", 128, True, True, "fp16"),
+]
+
+
+@pytest.mark.parametrize("v", WIDE_VARIANTS, ids=[v[0] for v in WIDE_VARIANTS])
+def test_linear_wide_tiles_sampled(W, v):
+    name, fmt, gs, has_z, has_g, dtype = v
+    K = 1152
+    G = 1 if gs == -1 else K // gs
+    lo, hi = (0.002, 0.02) if dtype == "fp16" else (0.001, 0.01)
+    for M, N in WIDE_TILE_SHAPES:
+        rng = seeded(505, K, N, G, int(has_z), int(has_g), len(name))
+        qweight = random_words(rng, (K, N // 8) if fmt == "awq" else (K // 8, N))
+        qzeros = random_words(rng, (G, N // 8)) if has_z else None
+        scales = uniform_scales(rng, (G, N), lo, hi, dtype)
+        g_idx = actorder_gidx(rng, K, gs) if has_g else None
+        Lyr = _prepare(W, fmt, K, N, gs, has_z, has_g, dtype, qweight, qzeros, scales, g_idx)
+        say(f"{name} M={M} N={N} kernel={Lyr.kernel_name(M)}")
+        x = normal_acts(seeded(506, M, K, N), (M, K), dtype)
+        y, guard = _run_linear(W, Lyr, x, guard_rows=4)
+        assert (guard.view(np.uint16) == 0x7F7F).all(), "write past row M"
+        ns = 2048
+        srng = seeded(507, M, N, len(name))
+        rows = np.concatenate([[0, M - 1, M - 1], srng.integers(0, M, size=ns - 3)])
+        cols = np.concatenate([[0, N - 1, 0], srng.integers(0, N, size=ns - 3)])
+        ref = O.reference_entries(x, fmt, dtype, qweight, qzeros, scales, gs, rows, cols, g_idx=g_idx)
+        _assert_close(y[rows, cols], ref, dtype, f"{name} M={M} N={N} (sampled {ns})")
+
+
+# ----------------------------------------------------------------------------
+# HIP graph capture: replays match the eager launch bit for bit
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [1, 16, 40, 300])
+def test_linear_hip_graph_replays_match_eager(W, M):
+    import torch
+    K, N, gs = 1152, 4096, 128
+    G = K // gs
+    rng = seeded(606, M)
+    qweight = random_words(rng, (K // 8, N))
+    qzeros = random_words(rng, (G, N // 8))
+    scales = uniform_scales(rng, (G, N), 0.002, 0.02, "fp16")
+    g_idx = actorder_gidx(rng, K, gs)
+    Lyr = _prepare(W, "std", K, N, gs, True, True, "fp16", qweight, qzeros, scales, g_idx)
+    say(f"graph M={M} kernel={Lyr.kernel_name(M)}")
+    x = to_dev(normal_acts(seeded(607, M), (M, K), "fp16"))
+    t = Lyr.tiled
+    ws_b = W.w4_workspace_size(Lyr.layer, M)
+    ws = torch.zeros((max(ws_b, 1),), dtype=torch.uint8, device="cuda")
+    y_eager = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    y_graph = torch.empty_like(y_eager)
+
+    def call(y):
+        W.w4a16_linear(Lyr.layer, M, x, t["qweight"], t["scales"], t["qzeros"], t["perm"], None, y,
+                       ws if ws_b else None, ws_b, torch.cuda.current_stream())
+
+    call(y_eager)
+    _sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(y_graph)
+    ref = to_host(y_eager).view(np.uint16)
+    for rep in range(3):
+        y_graph.fill_(0)                 # eager work between replays
+        _sync()
+        g.replay()
+        _sync()
+        assert np.array_equal(to_host(y_graph).view(np.uint16), ref), f"replay {rep}"

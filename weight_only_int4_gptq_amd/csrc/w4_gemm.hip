@@ -201,6 +201,7 @@ __device__ __forceinline__ void block_mac(f4 (&tot)[MT][NB], const u4 (&a)[MT][4
 // 16-row tile at xs + r * (K + kXPad); the pad of 8 halves moves consecutive
 // rows to different banks.
 constexpr int kXPad = 8;
+constexpr int kXlRows = 4;  // at most this many rows are staged (M <= 4)
 
 // Registers of one 128-row block: weights, scales and zeros of NB strips,
 // and (unless the activations come from LDS) the A operands of MT row tiles.
@@ -306,7 +307,7 @@ struct LaneView {
 };
 
 // Skinny kernel: see the header comment.  XL: activations staged in LDS.
-template <int MT, int NB, int KW, int GM, bool BF16, bool HAS_Z, bool HAS_PERM, bool XL>
+template <int MT, int NB, int KW, int GM, bool BF16, bool HAS_Z, bool HAS_PERM, bool XL, int D>
 __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restrict__ x, const u4* __restrict__ qw,
                                                         const uint16_t* __restrict__ sc,
                                                         const uint32_t* __restrict__ zs,
@@ -341,44 +342,60 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
 #pragma unroll
     for (int s = 0; s < NB; ++s) tot[i][s] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // Blocks are processed one at a time.  With LDS activations they are
-  // double buffered (the loads of block b + 1 are in flight while block b is
-  // computed) and the first block is issued before the staging so that its
-  // latency overlaps it; with register activations a single buffer keeps the
-  // register count, and so the occupancy, up (measured faster at M = 4..16).
-  // The steady-state loops contain no branch: the prefetch index is clamped
-  // to the wave's last block (one redundant in-bounds load at the end), so
-  // no branch join makes the compiler wait for every outstanding load.
+  // Blocks go through a D-deep register ring: the loads of blocks b + 1 ..
+  // b + D - 1 (weights, scales, zeros and, without LDS staging, the
+  // activations) are in flight while block b is computed, so a wave with at
+  // most D blocks pays one memory latency, not one per block.  With LDS
+  // activations the first blocks are issued before the staging so that
+  // their latency overlaps it.  The ring loops are fully unrolled (constant
+  // slot indices keep the ring in registers) and branch-free in steady
+  // state: the prefetch index is clamped to the wave's last block (redundant
+  // in-bounds loads at the end), so no branch join makes the compiler wait
+  // for every outstanding load.
+  static_assert(D >= 2, "ring depth");
   const bool has_blocks = lo < hi;  // wave-uniform
-  BlockRegs<MT, NB, NP, XL> ra, rb;
-  if (has_blocks) v.load_block(lo, ra);
+  const int last = hi - 1;
+  BlockRegs<MT, NB, NP, XL> ring[D];
+  if (has_blocks) {
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u) v.load_block(lo + u < last ? lo + u : last, ring[u]);
+  }
   if constexpr (XL) {
-    const int64_t rows = (M - m0) < 16 ? (M - m0) : 16;
+    // Stage the (at most kXlRows) activation rows: the loads of every row of
+    // a chunk column are issued before any is written, so one memory latency
+    // covers the whole chunk column (rows >= M are neither loaded nor
+    // written).
+    const int rows = (int)((M - m0) < kXlRows ? (M - m0) : kXlRows);
     const int64_t K8 = K / 8;
-    for (int64_t r = 0; r < rows; ++r) {
-      const uint16_t* src = x + (m0 + r) * K;
-      uint16_t* dst = xlds + r * (K + kXPad);
-      for (int64_t k8 = threadIdx.x; k8 < K8; k8 += 64 * KW) {
-        u4 val;
-        if constexpr (!HAS_PERM) {
-          val = *reinterpret_cast<const u4*>(src + 8 * k8);
-        } else {
-          const int4 p0 = *reinterpret_cast<const int4*>(perm + 8 * k8);
-          const int4 p1 = *reinterpret_cast<const int4*>(perm + 8 * k8 + 4);
-          const uint32_t idx[8] = {(uint32_t)p0.x, (uint32_t)p0.y, (uint32_t)p0.z, (uint32_t)p0.w,
-                                   (uint32_t)p1.x, (uint32_t)p1.y, (uint32_t)p1.z, (uint32_t)p1.w};
+    for (int64_t k8 = threadIdx.x; k8 < K8; k8 += 64 * KW) {
+      u4 val[kXlRows];
+      if constexpr (!HAS_PERM) {
+#pragma unroll
+        for (int r = 0; r < kXlRows; ++r)
+          if (r < rows) val[r] = *reinterpret_cast<const u4*>(x + (m0 + r) * K + 8 * k8);
+      } else {
+        const int4 p0 = *reinterpret_cast<const int4*>(perm + 8 * k8);
+        const int4 p1 = *reinterpret_cast<const int4*>(perm + 8 * k8 + 4);
+        const uint32_t idx[8] = {(uint32_t)p0.x, (uint32_t)p0.y, (uint32_t)p0.z, (uint32_t)p0.w,
+                                 (uint32_t)p1.x, (uint32_t)p1.y, (uint32_t)p1.z, (uint32_t)p1.w};
+#pragma unroll
+        for (int r = 0; r < kXlRows; ++r) {
+          if (r >= rows) continue;
+          const uint16_t* src = x + (m0 + r) * K;
           uint32_t h[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) h[e] = src[idx[e] < (uint32_t)K ? idx[e] : 0u];
-          val = u4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+          val[r] = u4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
         }
-        *reinterpret_cast<u4*>(dst + 8 * k8) = val;
       }
+#pragma unroll
+      for (int r = 0; r < kXlRows; ++r)
+        if (r < rows) *reinterpret_cast<u4*>(xlds + r * (K + kXPad) + 8 * k8) = val[r];
     }
     __syncthreads();
   }
 
-  auto compute = [&](int b, BlockRegs<MT, NB, NP, XL>& r) {
+  auto compute = [&](int b, BlockRegs<MT, NB, NP, XL>& r) __attribute__((always_inline)) {
     if constexpr (XL) {
       u4 a[MT][4];
       v.load_a_lds(b, a);
@@ -388,22 +405,18 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
     }
   };
   if (has_blocks) {
-    const int last = hi - 1;
     int kb = lo;
-    if constexpr (XL) {
-      for (; kb < last; kb += 2) {  // blocks kb and kb + 1 exist
-        v.load_block(kb + 1, rb);
-        compute(kb, ra);
-        v.load_block(kb + 2 < last ? kb + 2 : last, ra);
-        compute(kb + 1, rb);
-      }
-      if (kb == last) compute(kb, ra);  // odd count: ra holds the last block
-    } else {
-      for (; kb <= last; ++kb) {
-        compute(kb, ra);
-        v.load_block(kb + 1 < last ? kb + 1 : last, ra);
+    for (; kb + D <= hi; kb += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        const int nb = kb + u + D - 1;
+        v.load_block(nb < last ? nb : last, ring[(u + D - 1) % D]);
+        compute(kb + u, ring[u]);
       }
     }
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u)
+      if (kb + u < hi) compute(kb + u, ring[u]);
   }
 
   // Sum the KW waves' partial results in LDS, then bias, round and store.
@@ -442,20 +455,31 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Wide kernel (M > 16: LDS-staged activations)
+// Wide kernel (M > 16: LDS-staged activations, pipelined over K)
 //
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid; wave (wm, wn) owns MT
-// 16-row tiles and NS strips, so the workgroup tile is 32 MT x 32 NS.  Per
-// 128-row group of K:
-//   * the 32 MT x 128 activation tile is staged in LDS, double buffered, one
-//     barrier per group, by direct global->LDS loads (no registers): 16-byte
-//     chunk j of row r is stored at chunk position j ^ (r % 16) of the row,
-//     so the 16 rows that one A-operand read touches fall on distinct banks;
-//   * each wave streams the packed words of its NS strips straight from HBM
-//     into registers (one 16-byte load per strip per lane), prefetched one
-//     group ahead together with scales and zeros;
-//   * for each K step the NS strips are dequantized in registers and fed to
-//     MT x NS MFMAs.
+// Workgroup: WN waves side by side.  Every wave owns the same BM = 16 MT rows
+// and NS strips of its own, so the workgroup tile is 16 MT x 16 NS WN.  The
+// dequantization of a strip is shared by the MT row tiles of the wave, so a
+// tall wave tile keeps the vector ALU work per MFMA low.
+//
+// K is walked in 128-row blocks through an S-deep pipeline:
+//   * the BM x 128 activation tile of block b sits in LDS slot b % S, written
+//     by direct global->LDS loads (no registers): 16-byte chunk j of row r is
+//     stored at chunk position j ^ (r % 16), so the 16 rows that one
+//     A-operand read touches fall on distinct banks;
+//   * the packed words, scales and zeros of block b sit in register slot
+//     b % S of each wave.
+// Iteration b waits until its own block has landed (the loads of the S - 2
+// later blocks stay in flight), passes one barrier (every wave's part of the
+// tile is visible, and every wave is done with slot (b - 1) % S), issues the
+// loads of block b + S - 1 into that slot and computes block b.
+//
+// The wait is a vector-memory counter wait: at most kAfter = (S - 2) (NS + NA)
+// loads may remain outstanding, where NS word loads and NA direct-to-LDS
+// loads are issued per block by each wave.  The scale and zero loads of the
+// later blocks are not counted, which only makes the count smaller than the
+// number of loads truly issued after block b (the wait is never too short).
+//
 // Scaling uses one accumulator set per tile: at the start of scale period g
 // the fp32 accumulator (which holds sum_{h<g} P_h s_h / s_{g-1}) is
 // multiplied by s_{g-1} / s_g, the MFMAs then add the exact integer-weighted
@@ -463,74 +487,140 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
 // the end.  The tile layout never stores a zero scale (the repack replaces
 // it and zeroes the codes' contribution), so every ratio is finite; each
 // multiply adds one fp32 rounding (relative 2^-24 per period).
-// Rows >= M are staged from row M - 1 and never stored; strips >= N/16 are
-// skipped.  MT = 4, NS = 4 (128 x 128) serves prefill; smaller tiles give
-// mid-size M enough workgroups.
+// Rows >= M are staged from row M - 1 and never stored; strips >= N/16 read
+// strip 0 and are never stored.
 // ---------------------------------------------------------------------------
-constexpr int kWideThreads = 256;
-
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int MT, int NS, int GM, bool BF16, bool HAS_Z>
-__global__ __launch_bounds__(kWideThreads, 2) void gemm_wide(const uint16_t* __restrict__ x,
-                                                               const u4* __restrict__ qw,
-                                                               const uint16_t* __restrict__ sc,
-                                                               const uint32_t* __restrict__ zs,
-                                                               const uint16_t* __restrict__ bias,
-                                                               uint16_t* __restrict__ y, int64_t M, int64_t K,
-                                                               int64_t N, int G) {
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at dst + 16 l (dst is wave-uniform).
+__device__ __forceinline__ void load_lds16(const uint16_t* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+
+// Workgroup barrier for the pipeline.  __syncthreads() would add a release
+// fence, which waits for every outstanding direct-to-LDS load (they count as
+// LDS writes) and so drains the whole pipeline at every block.  Here each
+// wave has already waited for its own loads of the block about to be read
+// (wait_vmcnt), so the bare barrier suffices; the empty asm statements keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MT, int NS, int WN, int S>
+struct WideCfg {
+  static constexpr int BM = 16 * MT;          // rows per workgroup tile
+  static constexpr int BN = 16 * NS * WN;     // columns per workgroup tile
+  static constexpr int NA = BM / (4 * WN);    // direct-to-LDS loads per wave per block
+  static constexpr int kAfter = (S - 2) * (NS + NA);
+  static_assert(NA >= 1 && NA * 4 * WN == BM, "the activation tile splits evenly over the waves");
+  static_assert(S >= 2 && kAfter < 64, "pipeline depth");
+};
+
+template <int MT, int NS, int WN, int S, int GM, bool BF16, bool HAS_Z>
+__global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restrict__ x,
+                                                          const u4* __restrict__ qw,
+                                                          const uint16_t* __restrict__ sc,
+                                                          const uint32_t* __restrict__ zs,
+                                                          const uint16_t* __restrict__ bias,
+                                                          uint16_t* __restrict__ y, int64_t M, int64_t K,
+                                                          int64_t N, int G) {
+  using C = WideCfg<MT, NS, WN, S>;
   constexpr int NP = Groups<GM>::kPeriods, SP = Groups<GM>::kSteps;
-  constexpr int BM = 32 * MT;           // rows per workgroup tile
-  constexpr int STRIPS = 2 * NS;        // strips per workgroup tile
-  constexpr int kStage = BM / 16;       // staging loads per wave per group (4 rows each)
-  __shared__ __attribute__((aligned(1024))) uint16_t xs[2][BM * kTileK];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int c = lane & 15, quad = lane >> 4;
-  const int64_t T = N / kTileN;
-  const int64_t nblk = K / kTileK;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int64_t tw0 = (int64_t)blockIdx.x * STRIPS + NS * wn;  // first strip of this wave
-  const uint32_t zshift = 4u * (uint32_t)(c & 7);
-  const NibbleMasks nm = NibbleMasks::make();
-
-  // staging: instruction i of wave w fills rows (kStage w + i) * 4 .. + 3 of
-  // the tile; lane l lands at chunk position l % 16 of row base + l / 16 and
-  // so loads logical chunk (l % 16) ^ (row % 16).
-  auto stage = [&](int64_t kb, int buf) {
-#pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-      const int row0 = 4 * (kStage * wave + i);
-      const int row = row0 + (lane >> 4);
-      int64_t m = m0 + row;
-      m = m < M ? m : M - 1;
-      const int j = (lane & 15) ^ (row & 15);
-      const uint16_t* src = x + m * K + kb * kTileK + 8 * j;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)&xs[buf][row0 * kTileK], 16, 0, 0);
+  constexpr int NA = C::NA;
+  // One LDS array per pipeline slot (BM x 128 halves each).  Separate
+  // objects let the compiler tell the slots apart: a read of slot u then
+  // waits only for the direct-to-LDS loads into slot u, not for every such
+  // load in flight.
+  constexpr int kSlot = C::BM * kTileK, kNone = 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds0[kSlot];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds1[kSlot];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds2[S > 2 ? kSlot : kNone];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds3[S > 3 ? kSlot : kNone];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds4[S > 4 ? kSlot : kNone];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds5[S > 5 ? kSlot : kNone];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds6[S > 6 ? kSlot : kNone];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds7[S > 7 ? kSlot : kNone];
+  static_assert(S <= 8, "at most eight LDS slots");
+  auto slot_lds = [&](int u) __attribute__((always_inline)) -> uint16_t* {
+    switch (u) {
+      case 0: return lds0;
+      case 1: return lds1;
+      case 2: return lds2;
+      case 3: return lds3;
+      case 4: return lds4;
+      case 5: return lds5;
+      case 6: return lds6;
+      default: return lds7;
     }
   };
 
-  struct Meta {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, quad = lane >> 4;
+  const int64_t T = N / kTileN;
+  const int64_t nblk = K / kTileK;
+  const int64_t m0 = (int64_t)blockIdx.y * C::BM;
+  const int64_t tw0 = ((int64_t)blockIdx.x * WN + wave) * NS;  // first strip of this wave
+  const uint32_t zshift = 4u * (uint32_t)(c & 7);
+  const NibbleMasks nm = NibbleMasks::make();
+
+  // per-strip operand pointers (strips past the end read strip 0)
+  const u4* wp[NS];
+  const uint16_t* sp[NS];
+  const uint32_t* zp[NS];
+#pragma unroll
+  for (int nt = 0; nt < NS; ++nt) {
+    const int64_t t = tw0 + nt;
+    const int64_t tt = t < T ? t : 0;
+    wp[nt] = qw + tt * nblk * 64 + lane;
+    sp[nt] = sc + tt * G * kTileN + c;
+    zp[nt] = HAS_Z ? zs + tt * G * 2 + (c >> 3) : nullptr;
+  }
+  // staging: load i of this wave fills rows 4 (NA wave + i) .. + 3 of the
+  // tile; lane l lands at chunk position l % 16 of row base + l / 16 and so
+  // loads logical chunk (l % 16) ^ (row % 16)
+  const uint16_t* ap[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int row = 4 * (NA * wave + i) + quad;
+    int64_t m = m0 + row;
+    m = m < M ? m : M - 1;
+    ap[i] = x + m * K + 8 * (c ^ (row & 15));
+  }
+
+  struct Slot {
     u4 w[NS];
     uint16_t s[NS][NP];
     uint32_t z[NS][NP];
   };
-  auto load_meta = [&](int64_t kb, Meta& mt) {
+  Slot rg[S];
+
+  auto issue = [&](int64_t b, Slot& r, int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int nt = 0; nt < NS; ++nt) {
-      const int64_t t = tw0 + nt;
-      const bool ok = t < T;  // wave-uniform
-      const int64_t tt = ok ? t : 0;
-      mt.w[nt] = qw[(tt * nblk + kb) * 64 + lane];
+    for (int nt = 0; nt < NS; ++nt)
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const int64_t g = Groups<GM>::group((int)kb, p);
-        mt.s[nt][p] = sc[(tt * G + g) * kTileN + c];
-        mt.z[nt][p] = HAS_Z ? zs[(tt * G + g) * 2 + (c >> 3)] : 0u;
+        const int64_t g = Groups<GM>::group((int)b, p);
+        r.s[nt][p] = sp[nt][g * kTileN];
+        r.z[nt][p] = HAS_Z ? zp[nt][g * 2] : 0u;
       }
-    }
+#pragma unroll
+    for (int nt = 0; nt < NS; ++nt) r.w[nt] = wp[nt][b * 64];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) load_lds16(ap[i] + b * kTileK, slot_lds(slot) + 4 * (NA * wave + i) * kTileK);
   };
 
   f4 acc[MT][NS];
@@ -543,36 +633,26 @@ __global__ __launch_bounds__(kWideThreads, 2) void gemm_wide(const uint16_t* __r
 #pragma unroll
   for (int nt = 0; nt < NS; ++nt) s_prev[nt] = 1.f;
 
-  Meta cur, nxt;
-  stage(0, 0);
-  load_meta(0, cur);
-  __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of tile 0 have landed
-  for (int64_t kb = 0; kb < nblk; ++kb) {
-    const int buf = (int)(kb & 1);
-    __syncthreads();  // tile kb visible; buffer buf ^ 1 free
-    // prefetch (clamped at the last group: one redundant in-bounds load)
-    const int64_t kn = kb + 1 < nblk ? kb + 1 : kb;
-    stage(kn, buf ^ 1);
-    load_meta(kn, nxt);
-    // row of this lane in tile i: 16 (MT wm + i) + c, so row % 16 == c
-    const uint16_t* xa = &xs[buf][(16 * MT * wm + c) * kTileK];
+  auto compute = [&](const Slot& r, int slot) __attribute__((always_inline)) {
+    // row of this lane in tile i: 16 i + c, so row % 16 == c
+    const uint16_t* xa = slot_lds(slot) + c * kTileK;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       uint32_t n1[NS], n2[NS];
       float nzz[NS];
 #pragma unroll
       for (int nt = 0; nt < NS; ++nt) {
-        const uint32_t z = HAS_Z ? (cur.z[nt][p] >> zshift) & 0xFu : 8u;
+        const uint32_t z = HAS_Z ? (r.z[nt][p] >> zshift) & 0xFu : 8u;
         n1[nt] = nz1024_bits(z);
         n2[nt] = nz64_bits(z);
         nzz[nt] = -(128.0f + (float)z);
-        const float s_cur = act_to_f32<BF16>(cur.s[nt][p]);
+        const float s_cur = act_to_f32<BF16>(r.s[nt][p]);
         if constexpr (GM != GM_CH) {
-          const float r = s_prev[nt] * __builtin_amdgcn_rcpf(s_cur);
+          const float ratio = s_prev[nt] * __builtin_amdgcn_rcpf(s_cur);
 #pragma unroll
           for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][nt][q] *= r;
+            for (int q = 0; q < 4; ++q) acc[i][nt][q] *= ratio;
         }
         s_prev[nt] = s_cur;
       }
@@ -585,20 +665,21 @@ __global__ __launch_bounds__(kWideThreads, 2) void gemm_wide(const uint16_t* __r
       for (int j = p * SP; j < (p + 1) * SP; ++j) {
         u4 a[MT];
 #pragma unroll
-        for (int i = 0; i < MT; ++i) a[i] = *reinterpret_cast<const u4*>(xa + 16 * i * kTileK + 8 * ((4 * j + quad) ^ c));
+        for (int i = 0; i < MT; ++i)
+          a[i] = *reinterpret_cast<const u4*>(xa + 16 * i * kTileK + 8 * ((4 * j + quad) ^ c));
         if constexpr (BF16) {
 #pragma unroll
           for (int i = 0; i < MT; ++i) rs[i] = mfma<true>(a[i], ones, rs[i]);
         }
 #pragma unroll
         for (int nt = 0; nt < NS; ++nt) {
-          u4 b;
+          u4 bq;
           if constexpr (BF16)
-            b = dq_bf16(cur.w[nt][j], nm);
+            bq = dq_bf16(r.w[nt][j], nm);
           else
-            b = dq_f16(cur.w[nt][j], n1[nt], n2[nt], nm);
+            bq = dq_f16(r.w[nt][j], n1[nt], n2[nt], nm);
 #pragma unroll
-          for (int i = 0; i < MT; ++i) acc[i][nt] = mfma<BF16>(a[i], b, acc[i][nt]);
+          for (int i = 0; i < MT; ++i) acc[i][nt] = mfma<BF16>(a[i], bq, acc[i][nt]);
         }
       }
       if constexpr (BF16) {
@@ -611,9 +692,33 @@ __global__ __launch_bounds__(kWideThreads, 2) void gemm_wide(const uint16_t* __r
             for (int q = 0; q < 4; ++q) acc[i][nt][q] = __builtin_fmaf(nzz[nt], rs[i][q], acc[i][nt][q]);
       }
     }
-    cur = nxt;
-    __builtin_amdgcn_s_waitcnt(0);  // the next tile has landed before the barrier publishes it
+  };
+
+  // one pipeline iteration on block b, register/LDS slot U (compile time)
+  // (called with compile-time slots only: every loop around it is fully
+  // unrolled, so the slot arrays stay in registers)
+  auto iterate = [&](int64_t b, int u) __attribute__((always_inline)) {
+    const int un = (u + S - 1) % S;
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<C::kAfter>();
+    lds_barrier();
+    const int64_t bn = b + S - 1 < nblk ? b + S - 1 : nblk - 1;  // clamped: a redundant in-bounds load
+    issue(bn, rg[un], un);
+    compute(rg[u], u);
+  };
+
+  // prologue: blocks 0 .. S - 2 (clamped to the last block)
+#pragma unroll
+  for (int u = 0; u < S - 1; ++u) issue(u < nblk ? u : nblk - 1, rg[u], u);
+  int64_t b = 0;
+  for (; b + S <= nblk; b += S) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) iterate(b + u, u);
   }
+  // the last nblk % S blocks
+#pragma unroll
+  for (int u = 0; u < S - 1; ++u)
+    if (b + u < nblk) iterate(b + u, u);
 
   // epilogue: lane holds column c of each strip, rows 4 quad + r of each tile
 #pragma unroll
@@ -621,13 +726,13 @@ __global__ __launch_bounds__(kWideThreads, 2) void gemm_wide(const uint16_t* __r
     const int64_t t = tw0 + nt;
     if (t >= T) continue;
     const int64_t n = t * kTileN + c;
-    const float b = bias != nullptr ? act_to_f32<BF16>(bias[n]) : 0.f;
+    const float bv = bias != nullptr ? act_to_f32<BF16>(bias[n]) : 0.f;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + 16 * (MT * wm + i) + 4 * quad + r;
-        if (m < M) y[m * N + n] = f32_to_act<BF16>(acc[i][nt][r] * s_prev[nt] + b);
+        const int64_t m = m0 + 16 * i + 4 * quad + r;
+        if (m < M) y[m * N + n] = f32_to_act<BF16>(acc[i][nt][r] * s_prev[nt] + bv);
       }
   }
 }
@@ -663,15 +768,24 @@ constexpr size_t kMaxSkinnyLds = 64 * 1024;
 
 inline size_t skinny_lds_bytes(int mt, int nb, int kw, bool xl, int64_t M, int64_t K) {
   size_t b = (size_t)kw * mt * nb * 4 * 64 * sizeof(float);
-  if (xl) b += (size_t)(M < 16 ? M : 16) * (size_t)(K + kXPad) * sizeof(uint16_t);
+  if (xl) b += (size_t)(M < kXlRows ? M : kXlRows) * (size_t)(K + kXPad) * sizeof(uint16_t);
   return b;
 }
 
-template <int MT, int NB, int KW, int GM, bool BF16, bool HZ, bool HP, bool XL>
+// Ring depth of a skinny configuration (from timing sweeps): double
+// buffering with LDS activations, where deeper rings measured slower; three
+// or four blocks in flight when the activations come from registers.
+template <int MT, int NB, bool XL, bool HP>
+constexpr int skinny_depth() {
+  return XL ? 2 : (MT * NB == 1 ? 4 : (MT * NB == 2 ? 3 : 2));
+}
+
+template <int MT, int NB, int KW, int GM, bool BF16, bool HZ, bool HP, bool XL, int D = skinny_depth<MT, NB, XL, HP>()>
 hipError_t run_skinny(const Args& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.N / (kTileN * NB)), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
+  if (XL && a.M > kXlRows) return hipErrorInvalidValue;  // staging holds kXlRows rows
   const size_t lds = skinny_lds_bytes(MT, NB, KW, XL, a.M, a.K);
-  gemm_skinny<MT, NB, KW, GM, BF16, HZ, HP, XL><<<grid, 64 * KW, lds, st>>>(
+  gemm_skinny<MT, NB, KW, GM, BF16, HZ, HP, XL, D><<<grid, 64 * KW, lds, st>>>(
       a.x, a.qw, a.sc, a.zs, a.perm, a.bias, a.y, a.M, a.K, a.N, a.G);
   return hipGetLastError();
 }
@@ -691,29 +805,61 @@ hipError_t launch_gather(const uint16_t* x, const int32_t* perm, uint16_t* xp, i
   return hipGetLastError();
 }
 
-template <int MT, int NS, int GM, bool BF16, bool HZ>
+template <int MT, int NS, int WN, int S, int GM, bool BF16, bool HZ>
 hipError_t run_wide(const Args& a, const uint16_t* x, hipStream_t st) {
+  using C = WideCfg<MT, NS, WN, S>;
   const int64_t T = a.N / kTileN;
-  const dim3 grid((unsigned)((T + 2 * NS - 1) / (2 * NS)), (unsigned)((a.M + 32 * MT - 1) / (32 * MT)));
-  gemm_wide<MT, NS, GM, BF16, HZ><<<grid, kWideThreads, 0, st>>>(x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N,
-                                                                   a.G);
+  const dim3 grid((unsigned)((T + NS * WN - 1) / (NS * WN)), (unsigned)((a.M + C::BM - 1) / C::BM));
+  gemm_wide<MT, NS, WN, S, GM, BF16, HZ><<<grid, 64 * WN, 0, st>>>(x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K,
+                                                                   a.N, a.G);
   return hipGetLastError();
 }
 
-template <int MT, int NS, bool BF16, bool HZ>
+template <int MT, int NS, int WN, int S, bool BF16, bool HZ>
 hipError_t wide_gm(const Args& a, const uint16_t* x, hipStream_t st) {
   switch (group_mode(a.gs, a.K)) {
-    case GM_32: return run_wide<MT, NS, GM_32, BF16, HZ>(a, x, st);
-    case GM_64: return run_wide<MT, NS, GM_64, BF16, HZ>(a, x, st);
-    case GM_128: return run_wide<MT, NS, GM_128, BF16, HZ>(a, x, st);
-    default: return run_wide<MT, NS, GM_CH, BF16, HZ>(a, x, st);
+    case GM_32: return run_wide<MT, NS, WN, S, GM_32, BF16, HZ>(a, x, st);
+    case GM_64: return run_wide<MT, NS, WN, S, GM_64, BF16, HZ>(a, x, st);
+    case GM_128: return run_wide<MT, NS, WN, S, GM_128, BF16, HZ>(a, x, st);
+    default: return run_wide<MT, NS, WN, S, GM_CH, BF16, HZ>(a, x, st);
   }
 }
 
-template <int MT, int NS>
+template <int MT, int NS, int WN, int S>
 hipError_t wide_flags(const Shape& s, const Args& a, const uint16_t* x, hipStream_t st) {
-  if (s.bf16) return s.has_z ? wide_gm<MT, NS, true, true>(a, x, st) : wide_gm<MT, NS, true, false>(a, x, st);
-  return s.has_z ? wide_gm<MT, NS, false, true>(a, x, st) : wide_gm<MT, NS, false, false>(a, x, st);
+  if (s.bf16)
+    return s.has_z ? wide_gm<MT, NS, WN, S, true, true>(a, x, st) : wide_gm<MT, NS, WN, S, true, false>(a, x, st);
+  return s.has_z ? wide_gm<MT, NS, WN, S, false, true>(a, x, st) : wide_gm<MT, NS, WN, S, false, false>(a, x, st);
+}
+
+// Wide tile configurations: (MT, NS, WN, S) = row tiles per wave, strips per
+// wave, waves per workgroup, pipeline depth, and the smallest M each is used
+// for.  Chosen from timing sweeps of the prefill, mid-batch and act-order
+// shapes on MI355X; largest tile first.
+struct WideChoice {
+  int mt, ns, wn, st;
+  int64_t min_m;
+  const char* name;
+};
+constexpr WideChoice kWide[] = {
+    {4, 4, 4, 4, 1024, "w4_wide_64x256_s4"},
+    {4, 4, 4, 3, 0, "w4_wide_64x256_s3"},
+    {4, 2, 4, 4, 0, "w4_wide_64x128"},
+    {2, 2, 4, 8, 0, "w4_wide_32x128"},
+    {2, 2, 2, 8, 0, "w4_wide_32x64"},
+    {2, 1, 2, 8, 0, "w4_wide_32x32"},
+};
+constexpr int kNumWide = sizeof(kWide) / sizeof(kWide[0]);
+
+hipError_t wide_dispatch(int idx, const Shape& s, const Args& a, const uint16_t* x, hipStream_t st) {
+  switch (idx) {
+    case 0: return wide_flags<4, 4, 4, 4>(s, a, x, st);
+    case 1: return wide_flags<4, 4, 4, 3>(s, a, x, st);
+    case 2: return wide_flags<4, 2, 4, 4>(s, a, x, st);
+    case 3: return wide_flags<2, 2, 4, 8>(s, a, x, st);
+    case 4: return wide_flags<2, 2, 2, 8>(s, a, x, st);
+    default: return wide_flags<2, 1, 2, 8>(s, a, x, st);
+  }
 }
 
 // Act-order first gathers the columns of x into the workspace.
@@ -725,10 +871,7 @@ hipError_t launch_wide(const Shape& s, const GemmPlan& p, const Args& a, void* w
     if (e != hipSuccess) return e;
     x = xp;
   }
-  if (p.mt == 4) return p.nb == 4 ? wide_flags<4, 4>(s, a, x, st) : p.nb == 2 ? wide_flags<4, 2>(s, a, x, st)
-                                                                              : wide_flags<4, 1>(s, a, x, st);
-  if (p.mt == 2) return p.nb == 2 ? wide_flags<2, 2>(s, a, x, st) : wide_flags<2, 1>(s, a, x, st);
-  return p.nb == 2 ? wide_flags<1, 2>(s, a, x, st) : wide_flags<1, 1>(s, a, x, st);
+  return wide_dispatch(p.wide, s, a, x, st);
 }
 
 template <int MT, int NB, int KW, bool XL, bool BF16, bool HZ, bool HP>
@@ -760,33 +903,44 @@ hipError_t pick_flags(const Shape& s, const Args& a, hipStream_t st) {
 
 GemmPlan plan_gemm(const Shape& s, int64_t M) {
   // (mt, nb, kw, xl): 16-row tiles per wave, strips per workgroup, waves per
-  // workgroup (splitting K), activations staged in LDS.  Chosen from timing
-  // sweeps of the decode shapes on MI355X.  K is never split across
+  // workgroup (splitting K), activations staged in LDS; the ring depth
+  // follows from them (skinny_depth).  Chosen from timing sweeps of the
+  // decode shapes on MI355X.  K is never split across
   // workgroups: the agent-scope release fence that a cross-workgroup fix-up
   // needs writes back the XCD's whole L2 on gfx950 and cost far more than it
   // saved at these sizes (measured).
   GemmPlan p;
-  const bool deep_k = s.K >= 8192 || s.N <= 4096;  // few strips: more waves per strip
   const int64_t T = s.N / kTileN;
   if (M <= 4 && skinny_lds_bytes(1, 1, 8, true, M, s.K) <= kMaxSkinnyLds) {
-    const bool k16 = deep_k && skinny_lds_bytes(1, 1, 16, true, M, s.K) <= kMaxSkinnyLds;
+    // activations staged in LDS; few strips (N <= 8192): more waves per strip
+    const bool k16 = T <= 512 && skinny_lds_bytes(1, 1, 16, true, M, s.K) <= kMaxSkinnyLds;
     p = k16 ? GemmPlan{GemmKind::kSkinny, 1, 1, 16, true, "w4_skinny_lds_k16"}
             : GemmPlan{GemmKind::kSkinny, 1, 1, 8, true, "w4_skinny_lds_k8"};
   } else if (M <= 16) {
-    if (s.N >= 12288 && T % 4 == 0) p = GemmPlan{GemmKind::kSkinny, 1, 4, 16, false, "w4_skinny_n4_k16"};
-    else if (M <= 4 || s.K >= 8192) p = GemmPlan{GemmKind::kSkinny, 1, 1, 16, false, "w4_skinny_k16"};
-    else p = GemmPlan{GemmKind::kSkinny, 1, 1, 8, false, "w4_skinny_k8"};
+    // activations from registers; two strips per workgroup share them
+    // (halving the activation traffic) unless N is small and K long
+    if (T % 2 == 0 && (T >= 512 || s.K <= 4096)) {
+      p = s.K >= 8192 ? GemmPlan{GemmKind::kSkinny, 1, 2, 8, false, "w4_skinny_n2_k8"}
+                      : GemmPlan{GemmKind::kSkinny, 1, 2, 16, false, "w4_skinny_n2_k16"};
+    } else {
+      p = GemmPlan{GemmKind::kSkinny, 1, 1, 8, false, "w4_skinny_k8"};
+    }
   } else {
-    // wide kernel: wave tile mt x 16 rows by nb strips; the largest tile that
-    // still gives >= 512 workgroups (2 per CU), else the smallest
-    const int mt = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
-    const int64_t mtiles = (M + 32 * mt - 1) / (32 * mt);
-    int nb = mt == 4 ? 4 : 2;
-    while (nb > 1 && ((T + 2 * nb - 1) / (2 * nb)) * mtiles < 512) nb /= 2;
-    static const char* names[5][5] = {{}, {"", "w4_wide_32x32", "w4_wide_32x64"},
-                                      {"", "w4_wide_64x32", "w4_wide_64x64"}, {},
-                                      {"", "w4_wide_128x32", "w4_wide_128x64", "", "w4_wide_128x128"}};
-    p = GemmPlan{GemmKind::kWide, mt, nb, 4, false, names[mt][nb]};
+    // wide kernel: the largest tile that is not taller than M and still
+    // gives >= 256 workgroups (one per CU), else the smallest
+    int pick = kNumWide - 1;
+    for (int i = 0; i < kNumWide; ++i) {
+      const WideChoice& w = kWide[i];
+      const int64_t bm = 16 * w.mt, bn = 16 * w.ns * w.wn;
+      const int64_t wgs = ((s.N + bn - 1) / bn) * ((M + bm - 1) / bm);
+      if (M >= w.min_m && bm <= M && wgs >= 256) {
+        pick = i;
+        break;
+      }
+    }
+    const WideChoice& w = kWide[pick];
+    p = GemmPlan{GemmKind::kWide, w.mt, w.ns, w.wn, false, w.name};
+    p.wide = pick;
   }
   return p;
 }
@@ -828,8 +982,7 @@ hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* 
     sk.has_perm = false;
   }
   if (p.xl) return p.kw == 16 ? pick_flags<1, 1, 16, true>(sk, a, st) : pick_flags<1, 1, 8, true>(sk, a, st);
-  if (p.mt == 1 && p.nb == 4) return pick_flags<1, 4, 16, false>(sk, a, st);
-  if (p.mt == 1) return p.kw == 16 ? pick_flags<1, 1, 16, false>(sk, a, st) : pick_flags<1, 1, 8, false>(sk, a, st);
+  if (p.nb == 2) return p.kw == 16 ? pick_flags<1, 2, 16, false>(sk, a, st) : pick_flags<1, 2, 8, false>(sk, a, st);
   return pick_flags<1, 1, 8, false>(sk, a, st);
 }
 

@@ -55,6 +55,7 @@ struct GemmPlan {
   int kw;        // waves splitting K inside a workgroup
   bool xl;       // activations staged in LDS
   const char* name;
+  int wide = 0;  // wide tile configuration (index into the kernel's table)
 };
 
 GemmPlan plan_gemm(const Shape& s, int64_t M);
