@@ -214,10 +214,12 @@ struct BlockRegs {
 };
 
 // Per-lane view of the operands of one workgroup, with every pointer
-// computed once.  Lanes whose row is >= M read row M - 1 and select zero.
-// The selection is branch-free on purpose: an exec-masked load region here
-// let the compiler fold the row mask into the loop's active-lane mask, so
-// the next block's B operands were built for the masked lanes only.
+// computed once.  Lanes whose row is >= M read a valid row (M - 1, or row 0
+// of the LDS copy) unmasked: an output row of the MFMA depends only on its
+// own A row, and rows >= M are never stored.  The loads are unconditional on
+// purpose: an exec-masked load region here let the compiler fold the row
+// mask into the loop's active-lane mask, so the next block's B operands were
+// built for the masked lanes only.
 template <int MT, int NB, int GM, bool HAS_Z, bool HAS_PERM, bool XL>
 struct LaneView {
   static constexpr int NP = Groups<GM>::kPeriods;
@@ -249,13 +251,8 @@ struct LaneView {
       xr[i] = x + m * K + (HAS_PERM ? 0 : 8 * quad);
     }
     pm = perm + 8 * quad;
-    // LDS rows >= M are never staged; read row 0 instead (its value is discarded)
+    // LDS rows >= M are never staged; read row 0 instead
     xl = xlds + (row_ok[0] ? c : 0) * (K + kXPad) + 8 * quad;
-  }
-
-  __device__ static __forceinline__ u4 masked(bool ok, u4 v) {
-    const u4 z = {0u, 0u, 0u, 0u};
-    return ok ? v : z;
   }
 
   // A operands of block kb straight from global memory.
@@ -265,7 +262,7 @@ struct LaneView {
       const int k = kb * kTileK + 32 * j;
       if constexpr (!HAS_PERM) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i) a[i][j] = masked(row_ok[i], *reinterpret_cast<const u4*>(xr[i] + k));
+        for (int i = 0; i < MT; ++i) a[i][j] = *reinterpret_cast<const u4*>(xr[i] + k);
       } else {
         const int4 p0 = *reinterpret_cast<const int4*>(pm + k);
         const int4 p1 = *reinterpret_cast<const int4*>(pm + k + 4);
@@ -277,8 +274,7 @@ struct LaneView {
           uint32_t h[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) h[e] = xr[i][idx[e] < Ku ? idx[e] : 0u];
-          a[i][j] = masked(row_ok[i], u4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                                         h[6] | (h[7] << 16)});
+          a[i][j] = u4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
         }
       }
     }
@@ -287,7 +283,7 @@ struct LaneView {
   // A operands of block kb from the LDS copy (one row tile).
   __device__ __forceinline__ void load_a_lds(int kb, u4 (&a)[MT][4]) const {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a[0][j] = masked(row_ok[0], *reinterpret_cast<const u4*>(xl + kb * kTileK + 32 * j));
+    for (int j = 0; j < 4; ++j) a[0][j] = *reinterpret_cast<const u4*>(xl + kb * kTileK + 32 * j);
   }
 
   // Weights, scales, zeros (and global A operands) of block b.
@@ -848,8 +844,12 @@ constexpr WideChoice kWide[] = {
     {2, 2, 4, 8, 0, "w4_wide_32x128"},
     {2, 2, 2, 8, 0, "w4_wide_32x64"},
     {2, 1, 2, 8, 0, "w4_wide_32x32"},
+    // 16-row tiles, one wave per workgroup: M <= 16 on wide layers (below)
+    {1, 1, 1, 8, 0, "w4_wide_16x16"},
+    {1, 2, 1, 8, 0, "w4_wide_16x32"},
 };
-constexpr int kNumWide = sizeof(kWide) / sizeof(kWide[0]);
+constexpr int kNumWide = 6;  // entries searched for M > 16
+constexpr int kWide16x16 = 6, kWide16x32 = 7;
 
 hipError_t wide_dispatch(int idx, const Shape& s, const Args& a, const uint16_t* x, hipStream_t st) {
   switch (idx) {
@@ -858,7 +858,9 @@ hipError_t wide_dispatch(int idx, const Shape& s, const Args& a, const uint16_t*
     case 2: return wide_flags<4, 2, 4, 4>(s, a, x, st);
     case 3: return wide_flags<2, 2, 4, 8>(s, a, x, st);
     case 4: return wide_flags<2, 2, 2, 8>(s, a, x, st);
-    default: return wide_flags<2, 1, 2, 8>(s, a, x, st);
+    case 5: return wide_flags<2, 1, 2, 8>(s, a, x, st);
+    case 6: return wide_flags<1, 1, 1, 8>(s, a, x, st);
+    default: return wide_flags<1, 2, 1, 8>(s, a, x, st);
   }
 }
 
@@ -916,6 +918,13 @@ GemmPlan plan_gemm(const Shape& s, int64_t M) {
     const bool k16 = T <= 512 && skinny_lds_bytes(1, 1, 16, true, M, s.K) <= kMaxSkinnyLds;
     p = k16 ? GemmPlan{GemmKind::kSkinny, 1, 1, 16, true, "w4_skinny_lds_k16"}
             : GemmPlan{GemmKind::kSkinny, 1, 1, 8, true, "w4_skinny_lds_k8"};
+  } else if (M <= 16 && T >= 768) {
+    // many strips (N >= 12288): one wave per workgroup walks all of K with
+    // the activation tile in LDS, which measured faster than splitting K
+    const int idx = T <= 1024 ? kWide16x16 : kWide16x32;
+    const WideChoice& w = kWide[idx];
+    p = GemmPlan{GemmKind::kWide, w.mt, w.ns, w.wn, false, w.name};
+    p.wide = idx;
   } else if (M <= 16) {
     // activations from registers; two strips per workgroup share them
     // (halving the activation traffic) unless N is small and K long
