@@ -54,7 +54,7 @@ def parse():
     return p.parse_args()
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "skinny_decode_hbm_traffic.txt")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_decode_hbm_traffic.txt")
 GEMM_SOURCE = os.path.join(ROOT, "weight_only_int4_gptq_amd", "csrc", "w4_gemm.hip")
 
 
