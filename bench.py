@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--reps", type=int, default=0, help="launches per case for the per-kernel timing (0 = auto)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--compare", action="store_true",
+                   help="also time the unfused path (dense dequantization kernel, then torch.matmul) per case")
     p.add_argument("--eager", action="store_true",
                    help="time direct launches instead of HIP-graph replays (host launch cost included)")
     return p.parse_args()
@@ -245,6 +247,8 @@ def main():
     roof["per_launch_bytes_avg"] = round(sum_tb / len(per_case))
     roof["avg_launch_us"] = round(sum_us / len(per_case), 3)
 
+    unfused = compare_unfused(torch, runs, per_case, stream) if args.compare else None
+
     cpu = None if args.no_cpu else cpu_baseline(cases, args.cpu_seconds)
 
     for p in per_case:
@@ -276,11 +280,52 @@ def main():
         "tflops_step": round(flops_step / (ms_step * 1e-3) / 1e12, 3),
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
+        "dequant_then_gemm": unfused,
         "cpu_baseline": cpu,
         "per_case": per_case,
         "repack": repack,
     }
     print(json.dumps(out), flush=True)
+
+
+def compare_unfused(torch, runs, per_case, stream):
+    """The unfused path the pages describe for large batches: the library's
+    dense dequantization kernel writes W [K, N] in the activation dtype, then
+    torch.matmul (the vendor GEMM) computes x W.  Each part is timed with HIP
+    events over back-to-back direct launches, per case, next to the fused
+    kernel's time from the roofline timing."""
+    out = []
+    for r, pc in zip(runs, per_case):
+        lyr, M = r["lyr"], r["M"]
+        w = torch.empty((lyr.K, lyr.N), dtype=r["x"].dtype, device="cuda")
+        t = r["sets"][0]
+
+        def dq():
+            import weight_only_int4_gptq_amd as W
+            W.w4_dequant_dense(lyr.layer, t["qweight"], t["scales"], t["qzeros"], t["perm"], w, stream)
+
+        def mm():
+            torch.matmul(r["x"], w, out=r["y"])
+
+        res = {}
+        for name, fn in (("dequant_us", dq), ("gemm_us", mm)):
+            reps = 20 if M >= 1024 else 50
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) * 1e3 / reps
+        tot = res["dequant_us"] + res["gemm_us"]
+        out.append({"K": lyr.K, "N": lyr.N, "M": M, "dequant_us": round(res["dequant_us"], 3),
+                    "gemm_us": round(res["gemm_us"], 3), "unfused_us": round(tot, 3), "fused_us": pc["us"],
+                    "fused_speedup": round(tot / pc["us"], 3)})
+        del w
+    return out
 
 
 def cpu_baseline(cases, seconds):

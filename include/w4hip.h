@@ -161,6 +161,22 @@ w4_status w4a16_linear(const w4_layer* layer, int64_t M, const void* x, const in
                        const void* tiled_scales, const int32_t* tiled_qzeros, const int32_t* perm,
                        const void* bias, void* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Dense dequantization (the unfused path the fused GEMM is measured against).
+ * The vLLM AWQ practice page (section 5.3) runs large batches as "dequantize,
+ * then matmul" instead of the fused kernel; this call is the first half of
+ * that path.  It is not used by w4a16_linear.
+ *   tiled_*, perm  as written by w4_repack_gptq (perm NULL iff !has_g_idx)
+ *   w              act [K][N] row-major (device, 2-byte aligned) -- written:
+ *                  W[k][n] = (q[k][n] - z[g(k)][n]) * s[g(k)][n], computed
+ *                  exactly and rounded once (round to nearest even) to the
+ *                  activation dtype, rows in the original (unsorted) order.
+ *                  Zero scales give +0.
+ * Asynchronous on `stream`; every element of w is written once (a perm entry
+ * outside [0, K) -- impossible after a successful repack -- writes nothing).
+ * Errors as for w4a16_linear. */
+w4_status w4_dequant_dense(const w4_layer* layer, const int32_t* tiled_qweight, const void* tiled_scales,
+                           const int32_t* tiled_qzeros, const int32_t* perm, void* w, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

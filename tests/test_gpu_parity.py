@@ -453,3 +453,51 @@ def test_linear_hip_graph_replays_match_eager(W, M):
         g.replay()
         _sync()
         assert np.array_equal(to_host(y_graph).view(np.uint16), ref), f"replay {rep}"
+
+
+# ----------------------------------------------------------------------------
+# Dense dequantization (the unfused comparison path): exact
+# ----------------------------------------------------------------------------
+
+def _dense_expected(sw, sz, s, gs, dtype, gi):
+    """(q - z) s from the oracle, rounded once to the activation dtype, as
+    float64 values (so +0 and -0 compare equal)."""
+    q, z = O.codes_from_inputs("std", sw, sz)
+    K = q.shape[0]
+    Wd = O.dequant(q, z, O.act_to_f64(s, dtype), O.group_index(K, gs, gi))
+    if dtype == "fp16":
+        return Wd.astype(np.float16).astype(np.float64)
+    return O.bf16_to_f64(to_bf16_bits(Wd.astype(np.float32)))   # exact in fp32 (<= 15 significant bits)
+
+
+@pytest.mark.parametrize("v", REPACK_VARIANTS, ids=[v[0] for v in REPACK_VARIANTS])
+def test_dequant_dense_exact(W, v):
+    import torch
+    name, K, N, gs, has_z, has_g, dtype, zs = v
+    say(f"dequant_dense {name}")
+    sw, sz, s, gi = _std_layer_inputs(K, N, gs, has_z, has_g, dtype, zs)
+    Lyr = _prepare(W, "std", K, N, gs, has_z, has_g, dtype, sw, sz, s, gi)
+    expect = _dense_expected(sw, sz, s, gs, dtype, gi)
+    for fill in (0x00, 0xFF):
+        w = filled((K, N), act_dtype(dtype), fill)
+        Lyr.dequantize_dense(out=w)
+        _sync()
+        got = O.act_to_f64(to_host(w), dtype)
+        assert np.array_equal(got, expect), f"fill {fill:#x}"
+
+
+def test_dequant_then_matmul_matches_the_oracle(W):
+    import torch
+    # the unfused path: dense fp16 weight, then the library matmul
+    c = CONFIGS[0]
+    Lw = make_layer_inputs(c)
+    Lyr = _prepare(W, "awq", c.K, c.N, c.group_size, True, False, "fp16", Lw["qweight"], Lw["qzeros"],
+                   Lw["scales"], None)
+    Wd = Lyr.dequantize_dense()
+    for M in c.Ms:
+        say(f"dequant+matmul tiny M={M}")
+        x = make_acts(c, M)
+        y = torch.matmul(to_dev(x), Wd)
+        _sync()
+        ref = O.reference_linear(x, "awq", "fp16", Lw["qweight"], Lw["qzeros"], Lw["scales"], c.group_size)
+        _assert_close(to_host(y), ref, "fp16", f"dequant+matmul tiny M={M}")

@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
             "w4_repack_awq": ([P(w4_layer), VP, VP, VP, VP, VP], ctypes.c_int),
             "w4_repack_gptq": ([P(w4_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP], ctypes.c_int),
             "w4a16_linear": ([P(w4_layer), I64, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
+            "w4_dequant_dense": ([P(w4_layer), VP, VP, VP, VP, VP, VP], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -138,3 +139,10 @@ def w4a16_linear(layer, M, x, tiled_qweight, tiled_scales, tiled_qzeros, perm, b
     _raise("w4a16_linear", lib().w4a16_linear(
         ctypes.byref(layer), int(M), _ptr(x), _ptr(tiled_qweight), _ptr(tiled_scales), _ptr(tiled_qzeros),
         _ptr(perm), _ptr(bias), _ptr(y), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def w4_dequant_dense(layer, tiled_qweight, tiled_scales, tiled_qzeros, perm, w, stream=None) -> None:
+    """Dense W [K][N] in the activation dtype (the unfused comparison path)."""
+    _raise("w4_dequant_dense", lib().w4_dequant_dense(
+        ctypes.byref(layer), _ptr(tiled_qweight), _ptr(tiled_scales), _ptr(tiled_qzeros), _ptr(perm), _ptr(w),
+        _stream(stream)))

@@ -162,4 +162,22 @@ w4_status w4a16_linear(const w4_layer* L, int64_t M, const void* x, const int32_
   return W4_OK;
 }
 
+w4_status w4_dequant_dense(const w4_layer* L, const int32_t* tiled_qweight, const void* tiled_scales,
+                           const int32_t* tiled_qzeros, const int32_t* perm, void* w, void* stream) {
+  w4_status st = w4_check_layer(L);
+  if (st != W4_OK) return st;
+  const Shape s = w4::shape_of(L);
+  if (!tiled_qweight || !tiled_scales || !w) return W4_ERR_INVALID_ARGUMENT;
+  if (s.has_z != (tiled_qzeros != nullptr) || s.has_perm != (perm != nullptr)) return W4_ERR_INVALID_ARGUMENT;
+  if (!aligned(tiled_qweight, 16) || !aligned(tiled_scales, 2) || !aligned(w, 2) ||
+      (tiled_qzeros && !aligned(tiled_qzeros, 4)) || (perm && !aligned(perm, 4)))
+    return W4_ERR_INVALID_ARGUMENT;
+  st = device_status();
+  if (st != W4_OK) return st;
+  if (w4::launch_dequant_dense(s, tiled_qweight, tiled_scales, tiled_qzeros, perm, w,
+                               static_cast<hipStream_t>(stream)) != hipSuccess)
+    return W4_ERR_HIP;
+  return W4_OK;
+}
+
 }  // extern "C"

@@ -109,5 +109,16 @@ class W4A16Linear:
             self._ws = ws
         return ws
 
+    def dequantize_dense(self, out=None, stream=None) -> torch.Tensor:
+        """The dense weight W [K, N] in the activation dtype (for the unfused
+        dequantize-then-matmul comparison; the fused apply() never builds it)."""
+        if self.tiled is None:
+            raise RuntimeError("process_weights_after_loading has not run")
+        t = self.tiled
+        w = out if out is not None else torch.empty((self.K, self.N), dtype=t["scales"].dtype,
+                                                    device=t["qweight"].device)
+        A.w4_dequant_dense(self.layer, t["qweight"], t["scales"], t["qzeros"], t["perm"], w, stream)
+        return w
+
     def kernel_name(self, M: int) -> str:
         return A.w4_kernel_name(self.layer, M)
