@@ -372,10 +372,10 @@ def test_linear_full_size_sampled(W, c, M):
 # GEMM: every wide-kernel tile configuration, every group mode and dtype
 # ----------------------------------------------------------------------------
 
-# (M, N) pairs that select each wide tile of the kernel table (64x256 with a
-# 4- and a 3-deep pipeline, 64x128, 32x128, 32x64, and the one-wave 16x16 and
-# 16x32 tiles of M <= 16 on wide layers); K = 1152 is nine 128-row blocks, so
-# every pipeline depth runs full trips and a partial tail.
+# (M, N) pairs that select each wide tile of the kernel table (128x128,
+# 64x256, 64x128, 32x128, 32x64, and the one-wave 16x16 and 16x32 tiles of
+# M <= 16 on wide layers); K = 1152 is nine 128-row blocks, so every pipeline
+# depth runs full trips and a partial tail.
 WIDE_TILE_SHAPES = [(1024, 16384), (256, 16384), (64, 32768), (32, 32768), (40, 8192), (16, 12288),
                     (9, 20480)]
 WIDE_VARIANTS = [

@@ -831,14 +831,17 @@ hipError_t wide_flags(const Shape& s, const Args& a, const uint16_t* x, hipStrea
 // Wide tile configurations: (MT, NS, WN, S) = row tiles per wave, strips per
 // wave, waves per workgroup, pipeline depth, and the smallest M each is used
 // for.  Chosen from timing sweeps of the prefill, mid-batch and act-order
-// shapes on MI355X; largest tile first.
+// shapes on MI355X; largest tile first.  Prefill is bound by vector-ALU issue
+// (dequantization plus the per-period rescale, ~4 VALU instructions per MFMA
+// at 4 row tiles per wave), so its tile gives each wave 8 row tiles that
+// share one dequantization of each strip.
 struct WideChoice {
   int mt, ns, wn, st;
   int64_t min_m;
   const char* name;
 };
 constexpr WideChoice kWide[] = {
-    {4, 4, 4, 4, 1024, "w4_wide_64x256_s4"},
+    {8, 2, 4, 2, 1024, "w4_wide_128x128"},
     {4, 4, 4, 3, 0, "w4_wide_64x256_s3"},
     {4, 2, 4, 4, 0, "w4_wide_64x128"},
     {2, 2, 4, 8, 0, "w4_wide_32x128"},
@@ -853,7 +856,7 @@ constexpr int kWide16x16 = 6, kWide16x32 = 7;
 
 hipError_t wide_dispatch(int idx, const Shape& s, const Args& a, const uint16_t* x, hipStream_t st) {
   switch (idx) {
-    case 0: return wide_flags<4, 4, 4, 4>(s, a, x, st);
+    case 0: return wide_flags<8, 2, 4, 2>(s, a, x, st);
     case 1: return wide_flags<4, 4, 4, 3>(s, a, x, st);
     case 2: return wide_flags<4, 2, 4, 4>(s, a, x, st);
     case 3: return wide_flags<2, 2, 4, 8>(s, a, x, st);
