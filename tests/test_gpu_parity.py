@@ -373,10 +373,11 @@ def test_linear_full_size_sampled(W, c, M):
 # ----------------------------------------------------------------------------
 
 # (M, N) pairs that select each wide tile of the kernel table (128x128,
-# 64x256, 64x128, 32x128, 32x64, and the one-wave 16x16 and 16x32 tiles of
-# M <= 16 on wide layers); K = 1152 is nine 128-row blocks, so every pipeline
-# depth runs full trips and a partial tail.
-WIDE_TILE_SHAPES = [(1024, 16384), (256, 16384), (64, 32768), (32, 32768), (40, 8192), (16, 12288),
+# 64x256, 64x128, 32x128, the split-K 64x128 and 32x128 launches of M <= 64,
+# and the one-wave 16x16 and 16x32 tiles of M <= 16 on wide layers);
+# K = 1152 is nine 128-row blocks, so every pipeline depth runs full trips and
+# a partial tail, and a 4-way split gives uneven K ranges (2, 2, 2, 3).
+WIDE_TILE_SHAPES = [(1024, 16384), (256, 16384), (64, 32768), (32, 32768), (40, 8192), (24, 8192), (16, 12288),
                     (9, 20480)]
 WIDE_VARIANTS = [
     # (name, fmt, group_size, has_zeros, has_gidx, dtype)

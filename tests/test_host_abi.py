@@ -124,3 +124,22 @@ def test_repacks_reject_bad_arguments(W):
     act = W.make_layer(512, 256, 128, True, True, "fp16")
     assert g(ctypes.byref(act), 16, 16, 16, None, 16, 16, 16, 16, None, None) == W.W4_ERR_INVALID_ARGUMENT
     assert g(ctypes.byref(act), 16, 16, 16, 16, 16, 16, 16, 20, None, None) == W.W4_ERR_INVALID_ARGUMENT
+
+
+def test_split_k_workspace_is_sized_and_checked(W):
+    # mid-size M on a layer with N <= 16384 splits K over four workgroups:
+    # fp32 partials [4][M][N] live in the workspace
+    L = W.make_layer(8192, 8192, 128, False, False, "bf16")
+    assert W.w4_kernel_name(L, 32).endswith("splitk")
+    assert W.w4_workspace_size(L, 32) == 4 * 32 * 8192 * 4
+    assert W.w4_workspace_size(L, 64) == 4 * 64 * 8192 * 4
+    assert W.w4_workspace_size(L, 1) == 0 and W.w4_workspace_size(L, 2048) == 0
+    # a longer K splits eight ways
+    assert W.w4_workspace_size(W.make_layer(28672, 8192, 128, False, False, "bf16"), 32) == 8 * 32 * 8192 * 4
+    # act-order: the gathered activations (256-byte aligned) come first
+    La = W.make_layer(8192, 8192, 128, True, True, "fp16")
+    assert W.w4_workspace_size(La, 64) == 64 * 8192 * 2 + 4 * 64 * 8192 * 4
+    # too small a workspace is refused before any launch
+    need = W.w4_workspace_size(L, 32)
+    assert _lin(W, L, 32, qz=None, ws=16, ws_bytes=need - 1) == W.W4_ERR_WORKSPACE
+    assert _lin(W, L, 32, qz=None, ws=None, ws_bytes=0) == W.W4_ERR_WORKSPACE

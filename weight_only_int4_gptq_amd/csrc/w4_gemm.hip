@@ -531,8 +531,8 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
                                                           const uint16_t* __restrict__ sc,
                                                           const uint32_t* __restrict__ zs,
                                                           const uint16_t* __restrict__ bias,
-                                                          uint16_t* __restrict__ y, int64_t M, int64_t K,
-                                                          int64_t N, int G) {
+                                                          uint16_t* __restrict__ y, float* __restrict__ part,
+                                                          int64_t M, int64_t K, int64_t N, int G) {
   using C = WideCfg<MT, NS, WN, S>;
   constexpr int NP = Groups<GM>::kPeriods, SP = Groups<GM>::kSteps;
   constexpr int NA = C::NA;
@@ -568,6 +568,10 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
   const int c = lane & 15, quad = lane >> 4;
   const int64_t T = N / kTileN;
   const int64_t nblk = K / kTileK;
+  // split-K: workgroup z of gridDim.z walks blocks [kb0, kb0 + nb) (nb >= 1:
+  // the host never splits finer than one block)
+  const int64_t kb0 = nblk * blockIdx.z / gridDim.z;
+  const int64_t nb = nblk * (blockIdx.z + 1) / gridDim.z - kb0;
   const int64_t m0 = (int64_t)blockIdx.y * C::BM;
   const int64_t tw0 = ((int64_t)blockIdx.x * WN + wave) * NS;  // first strip of this wave
   const uint32_t zshift = 4u * (uint32_t)(c & 7);
@@ -698,38 +702,76 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<C::kAfter>();
     lds_barrier();
-    const int64_t bn = b + S - 1 < nblk ? b + S - 1 : nblk - 1;  // clamped: a redundant in-bounds load
-    issue(bn, rg[un], un);
+    const int64_t bn = b + S - 1 < nb ? b + S - 1 : nb - 1;  // clamped: a redundant in-bounds load
+    issue(kb0 + bn, rg[un], un);
     compute(rg[u], u);
   };
 
-  // prologue: blocks 0 .. S - 2 (clamped to the last block)
+  // prologue: blocks 0 .. S - 2 of the range (clamped to its last block)
 #pragma unroll
-  for (int u = 0; u < S - 1; ++u) issue(u < nblk ? u : nblk - 1, rg[u], u);
+  for (int u = 0; u < S - 1; ++u) issue(kb0 + (u < nb ? u : nb - 1), rg[u], u);
   int64_t b = 0;
-  for (; b + S <= nblk; b += S) {
+  for (; b + S <= nb; b += S) {
 #pragma unroll
     for (int u = 0; u < S; ++u) iterate(b + u, u);
   }
-  // the last nblk % S blocks
+  // the last nb % S blocks
 #pragma unroll
   for (int u = 0; u < S - 1; ++u)
-    if (b + u < nblk) iterate(b + u, u);
+    if (b + u < nb) iterate(b + u, u);
 
-  // epilogue: lane holds column c of each strip, rows 4 quad + r of each tile
+  // epilogue: lane holds column c of each strip, rows 4 quad + r of each tile;
+  // with split-K the fp32 partial goes to part[z][m][n] (bias and rounding
+  // happen in split_reduce)
+  float* pz = part != nullptr ? part + (int64_t)blockIdx.z * M * N : nullptr;
 #pragma unroll
   for (int nt = 0; nt < NS; ++nt) {
     const int64_t t = tw0 + nt;
     if (t >= T) continue;
     const int64_t n = t * kTileN + c;
-    const float bv = bias != nullptr ? act_to_f32<BF16>(bias[n]) : 0.f;
+    const float bv = bias != nullptr && pz == nullptr ? act_to_f32<BF16>(bias[n]) : 0.f;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t m = m0 + 16 * i + 4 * quad + r;
-        if (m < M) y[m * N + n] = f32_to_act<BF16>(acc[i][nt][r] * s_prev[nt] + bv);
+        if (m >= M) continue;
+        const float v = acc[i][nt][r] * s_prev[nt];
+        if (pz != nullptr)
+          pz[m * N + n] = v;
+        else
+          y[m * N + n] = f32_to_act<BF16>(v + bv);
       }
+  }
+}
+
+// y[m][n] = round(sum_z part[z][m][n] + bias[n]) for split-K launches; four
+// consecutive columns per thread (N is a multiple of 16).
+template <bool BF16>
+__global__ void split_reduce(const float* __restrict__ part, const uint16_t* __restrict__ bias,
+                             uint16_t* __restrict__ y, int64_t M, int64_t N, int splits) {
+  const int64_t total4 = M * N / 4, plane4 = total4;
+  const float4* p4 = reinterpret_cast<const float4*>(part);
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total4;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    float4 a = p4[idx];
+    for (int z = 1; z < splits; ++z) {
+      const float4 b = p4[z * plane4 + idx];
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    const int64_t n = (idx * 4) % N;
+    if (bias != nullptr) {
+      a.x += act_to_f32<BF16>(bias[n]);
+      a.y += act_to_f32<BF16>(bias[n + 1]);
+      a.z += act_to_f32<BF16>(bias[n + 2]);
+      a.w += act_to_f32<BF16>(bias[n + 3]);
+    }
+    const uint32_t lo = (uint32_t)f32_to_act<BF16>(a.x) | ((uint32_t)f32_to_act<BF16>(a.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_act<BF16>(a.z) | ((uint32_t)f32_to_act<BF16>(a.w) << 16);
+    reinterpret_cast<uint2*>(y)[idx] = make_uint2(lo, hi);
   }
 }
 
@@ -754,6 +796,8 @@ struct Args {
   const int32_t* perm;
   const uint16_t* bias;
   uint16_t* y;
+  float* part;  // split-K partials [splits][M][N] (workspace), or nullptr
+  int splits;   // K ranges (gridDim.z); 1 = no split
   int64_t M, K, N;
   int G, gs;
 };
@@ -805,9 +849,18 @@ template <int MT, int NS, int WN, int S, int GM, bool BF16, bool HZ>
 hipError_t run_wide(const Args& a, const uint16_t* x, hipStream_t st) {
   using C = WideCfg<MT, NS, WN, S>;
   const int64_t T = a.N / kTileN;
-  const dim3 grid((unsigned)((T + NS * WN - 1) / (NS * WN)), (unsigned)((a.M + C::BM - 1) / C::BM));
-  gemm_wide<MT, NS, WN, S, GM, BF16, HZ><<<grid, 64 * WN, 0, st>>>(x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K,
-                                                                   a.N, a.G);
+  const int splits = a.splits > 1 ? a.splits : 1;
+  if (splits > 1 && (a.part == nullptr || splits > a.K / kTileK)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((T + NS * WN - 1) / (NS * WN)), (unsigned)((a.M + C::BM - 1) / C::BM),
+                  (unsigned)splits);
+  gemm_wide<MT, NS, WN, S, GM, BF16, HZ><<<grid, 64 * WN, 0, st>>>(
+      x, a.qw, a.sc, a.zs, a.bias, a.y, splits > 1 ? a.part : nullptr, a.M, a.K, a.N, a.G);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t total4 = a.M * a.N / 4;
+  int64_t blocks = (total4 + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  split_reduce<BF16><<<(unsigned)blocks, 256, 0, st>>>(a.part, a.bias, a.y, a.M, a.N, splits);
   return hipGetLastError();
 }
 
@@ -867,8 +920,15 @@ hipError_t wide_dispatch(int idx, const Shape& s, const Args& a, const uint16_t*
   }
 }
 
+// Workspace of a call: the gathered activations (act-order, every path but
+// the LDS-staged skinny kernel) first, then the split-K partials.
+inline size_t gather_bytes(const Shape& s, const GemmPlan& p, int64_t M) {
+  return s.has_perm && !p.xl ? ((size_t)M * (size_t)s.K * sizeof(uint16_t) + 255) / 256 * 256 : 0;
+}
+
 // Act-order first gathers the columns of x into the workspace.
-hipError_t launch_wide(const Shape& s, const GemmPlan& p, const Args& a, void* ws, hipStream_t st) {
+hipError_t launch_wide(const Shape& s, const GemmPlan& p, const Args& a0, void* ws, hipStream_t st) {
+  Args a = a0;
   const uint16_t* x = a.x;
   if (s.has_perm) {
     uint16_t* xp = static_cast<uint16_t*>(ws);
@@ -876,6 +936,8 @@ hipError_t launch_wide(const Shape& s, const GemmPlan& p, const Args& a, void* w
     if (e != hipSuccess) return e;
     x = xp;
   }
+  a.splits = p.splits;
+  a.part = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + gather_bytes(s, p, a.M)) : nullptr;
   return wide_dispatch(p.wide, s, a, x, st);
 }
 
@@ -939,7 +1001,24 @@ GemmPlan plan_gemm(const Shape& s, int64_t M) {
     }
   } else {
     // wide kernel: the largest tile that is not taller than M and still
-    // gives >= 256 workgroups (one per CU), else the smallest
+    // gives >= 256 workgroups (one per CU), else the smallest.  Mid-size M
+    // (<= 64, bandwidth-bound) on layers with N <= 16384 instead splits K
+    // over 4 or 8 workgroups per tile (fp32 partials in the workspace, summed
+    // by split_reduce): more weight streams in flight, measured 1.35-2x
+    // faster than any unsplit tile there.
+    const int64_t nblk = s.K / kTileK;
+    if (M <= 64 && T <= 1024 && nblk >= 4) {
+      const int idx = M <= 32 ? 3 : 2;  // 32x128 or 64x128
+      int splits = s.K >= 16384 ? 8 : 4;
+      while (splits > 1 && splits * 2 > nblk) splits /= 2;  // >= 2 blocks per split
+      const WideChoice& w = kWide[idx];
+      p = GemmPlan{GemmKind::kWide, w.mt, w.ns, w.wn, false, splits > 1 ? (M <= 32 ? "w4_wide_32x128_splitk"
+                                                                                     : "w4_wide_64x128_splitk")
+                                                                        : w.name};
+      p.wide = idx;
+      p.splits = splits;
+      return p;
+    }
     int pick = kNumWide - 1;
     for (int i = 0; i < kNumWide; ++i) {
       const WideChoice& w = kWide[i];
@@ -959,10 +1038,9 @@ GemmPlan plan_gemm(const Shape& s, int64_t M) {
 
 size_t gemm_workspace_bytes(const Shape& s, int64_t M) {
   const GemmPlan p = plan_gemm(s, M);
-  // act-order: every path except the LDS-staged skinny kernel gathers the
-  // columns of x into the workspace first
-  if (s.has_perm && !p.xl) return (size_t)M * (size_t)s.K * sizeof(uint16_t);
-  return 0;
+  const size_t part = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)s.N * sizeof(float) : 0;
+  const size_t total = gather_bytes(s, p, M) + part;
+  return total;
 }
 
 hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* tiled_w, const void* tiled_s,
@@ -976,6 +1054,8 @@ hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* 
   a.perm = perm;
   a.bias = static_cast<const uint16_t*>(bias);
   a.y = static_cast<uint16_t*>(y);
+  a.part = nullptr;
+  a.splits = 1;
   a.M = M;
   a.K = s.K;
   a.N = s.N;

@@ -55,7 +55,8 @@ struct GemmPlan {
   int kw;        // waves splitting K inside a workgroup
   bool xl;       // activations staged in LDS
   const char* name;
-  int wide = 0;  // wide tile configuration (index into the kernel's table)
+  int wide = 0;    // wide tile configuration (index into the kernel's table)
+  int splits = 1;  // wide kernel: K ranges reduced by a second kernel (1 = none)
 };
 
 GemmPlan plan_gemm(const Shape& s, int64_t M);
