@@ -804,7 +804,7 @@ struct Args {
 
 // LDS bytes of a skinny launch: the reduction buffer, plus the staged
 // activation rows (at most 16, row stride K + kXPad halves) when XL.
-constexpr size_t kMaxSkinnyLds = 64 * 1024;
+constexpr size_t kMaxSkinnyLds = 128 * 1024;  // of the CU's 160 KiB
 
 inline size_t skinny_lds_bytes(int mt, int nb, int kw, bool xl, int64_t M, int64_t K) {
   size_t b = (size_t)kw * mt * nb * 4 * 64 * sizeof(float);
@@ -825,6 +825,14 @@ hipError_t run_skinny(const Args& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.N / (kTileN * NB)), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
   if (XL && a.M > kXlRows) return hipErrorInvalidValue;  // staging holds kXlRows rows
   const size_t lds = skinny_lds_bytes(MT, NB, KW, XL, a.M, a.K);
+  if (lds > kMaxSkinnyLds) return hipErrorInvalidValue;
+  if (lds > 64 * 1024) {
+    // dynamic LDS beyond 64 KiB has to be allowed per kernel (once)
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_skinny<MT, NB, KW, GM, BF16, HZ, HP, XL, D>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxSkinnyLds);
+    if (attr != hipSuccess) return attr;
+  }
   gemm_skinny<MT, NB, KW, GM, BF16, HZ, HP, XL, D><<<grid, 64 * KW, lds, st>>>(
       a.x, a.qw, a.sc, a.zs, a.perm, a.bias, a.y, a.M, a.K, a.N, a.G);
   return hipGetLastError();
