@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--reps", type=int, default=0, help="launches per case for the per-kernel timing (0 = auto)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--group-size", type=int, default=0, choices=[0, 32, 64, 128, -1],
+                   help="run the workload's shapes with this group size instead (0 = the workload's own)")
     p.add_argument("--compare", action="store_true",
                    help="also time the unfused path (dense dequantization kernel, then torch.matmul) per case")
     p.add_argument("--eager", action="store_true",
@@ -112,6 +114,10 @@ def main():
     W.lib()
     cfg_id = {"tiny": 1, "decode": 2, "mid": 3, "prefill": 4, "actorder": 5}[args.config]
     cases = [c for c in CONFIGS if c.cfg_id == cfg_id]
+    if args.group_size:
+        import dataclasses
+        cases = [dataclasses.replace(c, group_size=args.group_size, has_gidx=c.has_gidx and args.group_size != -1)
+                 for c in cases]
     stream = torch.cuda.current_stream()
 
     # ---- one-time repack (timed separately) and rotated weight copies ----

@@ -405,13 +405,14 @@ def test_linear_wide_tiles_sampled(W, v):
         Lyr = _prepare(W, fmt, K, N, gs, has_z, has_g, dtype, qweight, qzeros, scales, g_idx)
         say(f"{name} M={M} N={N} kernel={Lyr.kernel_name(M)}")
         x = normal_acts(seeded(506, M, K, N), (M, K), dtype)
-        y, guard = _run_linear(W, Lyr, x, guard_rows=4)
+        bias = uniform_scales(seeded(508, N), (N,), -1.0, 1.0, dtype) if name.startswith("awq") else None
+        y, guard = _run_linear(W, Lyr, x, bias, guard_rows=4)
         assert (guard.view(np.uint16) == 0x7F7F).all(), "write past row M"
         ns = 2048
         srng = seeded(507, M, N, len(name))
         rows = np.concatenate([[0, M - 1, M - 1], srng.integers(0, M, size=ns - 3)])
         cols = np.concatenate([[0, N - 1, 0], srng.integers(0, N, size=ns - 3)])
-        ref = O.reference_entries(x, fmt, dtype, qweight, qzeros, scales, gs, rows, cols, g_idx=g_idx)
+        ref = O.reference_entries(x, fmt, dtype, qweight, qzeros, scales, gs, rows, cols, g_idx=g_idx, bias=bias)
         _assert_close(y[rows, cols], ref, dtype, f"{name} M={M} N={N} (sampled {ns})")
 
 
@@ -502,3 +503,27 @@ def test_dequant_then_matmul_matches_the_oracle(W):
         _sync()
         ref = O.reference_linear(x, "awq", "fp16", Lw["qweight"], Lw["qzeros"], Lw["scales"], c.group_size)
         _assert_close(to_host(y), ref, "fp16", f"dequant+matmul tiny M={M}")
+
+
+# ----------------------------------------------------------------------------
+# Smallest layers: one 128-row block, one strip, every kernel family
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_linear_smallest_layers(W, dtype):
+    for K, N in ((128, 16), (256, 32), (128, 4096)):
+        rng = seeded(808, K, N, len(dtype))
+        G = K // 128
+        qweight = random_words(rng, (K // 8, N))
+        qzeros = random_words(rng, (G, N // 8))
+        lo, hi = (0.002, 0.02) if dtype == "fp16" else (0.001, 0.01)
+        scales = uniform_scales(rng, (G, N), lo, hi, dtype)
+        bias = uniform_scales(rng, (N,), -1.0, 1.0, dtype)
+        Lyr = _prepare(W, "std", K, N, 128, True, False, dtype, qweight, qzeros, scales, None)
+        for M in (1, 5, 16, 17, 40, 100, 1100):
+            say(f"smallest K={K} N={N} M={M} {dtype} kernel={Lyr.kernel_name(M)}")
+            x = normal_acts(seeded(809, M, K, N), (M, K), dtype)
+            ref = O.reference_linear(x, "std", dtype, qweight, qzeros, scales, 128, bias=bias)
+            y, guard = _run_linear(W, Lyr, x, bias, guard_rows=3)
+            assert (guard.view(np.uint16) == 0x7F7F).all(), "write past row M"
+            _assert_close(y, ref, dtype, f"smallest K={K} N={N} M={M}")
