@@ -377,8 +377,8 @@ def test_linear_full_size_sampled(W, c, M):
 # and the one-wave 16x16 and 16x32 tiles of M <= 16 on wide layers);
 # K = 1152 is nine 128-row blocks, so every pipeline depth runs full trips and
 # a partial tail, and a 4-way split gives uneven K ranges (2, 2, 2, 3).
-WIDE_TILE_SHAPES = [(1024, 16384), (256, 16384), (64, 32768), (32, 32768), (40, 8192), (24, 8192), (16, 12288),
-                    (9, 20480)]
+WIDE_TILE_SHAPES = [(1024, 16384), (256, 32768), (64, 32768), (32, 32768), (40, 8192), (24, 8192), (200, 8192),
+                    (16, 12288), (9, 20480)]
 WIDE_VARIANTS = [
     # (name, fmt, group_size, has_zeros, has_gidx, dtype)
     ("awq-fp16-g128", "awq", 128, True, False, "fp16"),

@@ -133,9 +133,14 @@ def test_split_k_workspace_is_sized_and_checked(W):
     assert W.w4_kernel_name(L, 32).endswith("splitk")
     assert W.w4_workspace_size(L, 32) == 4 * 32 * 8192 * 4
     assert W.w4_workspace_size(L, 64) == 4 * 64 * 8192 * 4
+    assert W.w4_workspace_size(L, 128) == 4 * 128 * 8192 * 4
     assert W.w4_workspace_size(L, 1) == 0 and W.w4_workspace_size(L, 2048) == 0
-    # a longer K splits eight ways
-    assert W.w4_workspace_size(W.make_layer(28672, 8192, 128, False, False, "bf16"), 32) == 8 * 32 * 8192 * 4
+    # a longer K splits eight ways (four at M = 256)
+    L2 = W.make_layer(28672, 8192, 128, False, False, "bf16")
+    assert W.w4_workspace_size(L2, 32) == 8 * 32 * 8192 * 4
+    assert W.w4_workspace_size(L2, 256) == 4 * 256 * 8192 * 4
+    # N = 57344 has workgroups enough: no split
+    assert W.w4_workspace_size(W.make_layer(8192, 57344, 128, False, False, "bf16"), 128) == 0
     # act-order: the gathered activations (256-byte aligned) come first
     La = W.make_layer(8192, 8192, 128, True, True, "fp16")
     assert W.w4_workspace_size(La, 64) == 64 * 8192 * 2 + 4 * 64 * 8192 * 4

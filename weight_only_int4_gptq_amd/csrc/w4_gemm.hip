@@ -987,8 +987,8 @@ GemmPlan plan_gemm(const Shape& s, int64_t M) {
   GemmPlan p;
   const int64_t T = s.N / kTileN;
   if (M <= 4 && skinny_lds_bytes(1, 1, 8, true, M, s.K) <= kMaxSkinnyLds) {
-    // activations staged in LDS; few strips (N <= 8192): more waves per strip
-    const bool k16 = T <= 512 && skinny_lds_bytes(1, 1, 16, true, M, s.K) <= kMaxSkinnyLds;
+    // activations staged in LDS; few strips (N <= 4096): more waves per strip
+    const bool k16 = T <= 256 && skinny_lds_bytes(1, 1, 16, true, M, s.K) <= kMaxSkinnyLds;
     p = k16 ? GemmPlan{GemmKind::kSkinny, 1, 1, 16, true, "w4_skinny_lds_k16"}
             : GemmPlan{GemmKind::kSkinny, 1, 1, 8, true, "w4_skinny_lds_k8"};
   } else if (M <= 16 && T >= 768) {
@@ -1008,31 +1008,35 @@ GemmPlan plan_gemm(const Shape& s, int64_t M) {
       p = GemmPlan{GemmKind::kSkinny, 1, 1, 8, false, "w4_skinny_k8"};
     }
   } else {
-    // wide kernel: the largest tile that is not taller than M and still
-    // gives >= 256 workgroups (one per CU), else the smallest.  Mid-size M
-    // (<= 64, bandwidth-bound) on layers with N <= 16384 instead splits K
-    // over 4 or 8 workgroups per tile (fp32 partials in the workspace, summed
-    // by split_reduce): more weight streams in flight, measured 1.35-2x
-    // faster than any unsplit tile there.
+    // wide kernel: the largest tile that is not taller than M (32 rows at
+    // least) and still gives >= 256 workgroups (one per CU), else the
+    // smallest.  Mid-size M
+    // (<= 256) on layers with N <= 16384 instead splits K over 4 or 8
+    // workgroups per tile (fp32 partials in the workspace, summed by
+    // split_reduce): enough workgroups and weight streams in flight; measured
+    // 1.35-2x faster at M <= 64 and 1.1-1.45x at M = 128/256 than any
+    // unsplit tile there.
     const int64_t nblk = s.K / kTileK;
-    if (M <= 64 && T <= 1024 && nblk >= 4) {
-      const int idx = M <= 32 ? 3 : 2;  // 32x128 or 64x128
-      int splits = s.K >= 16384 ? 8 : 4;
+    if (M <= 256 && T <= 1024 && nblk >= 4) {
+      // 32x128 (M <= 32), 64x128, or 64x256 for long K at M > 64
+      const int idx = M <= 32 ? 3 : (M > 64 && s.K >= 16384 ? 1 : 2);
+      int splits = M > 64 ? (s.K >= 16384 && M <= 128 ? 8 : 4) : (s.K >= 16384 ? 8 : 4);
       while (splits > 1 && splits * 2 > nblk) splits /= 2;  // >= 2 blocks per split
+      static const char* split_names[] = {"", "w4_wide_64x256_splitk", "w4_wide_64x128_splitk",
+                                          "w4_wide_32x128_splitk"};
       const WideChoice& w = kWide[idx];
-      p = GemmPlan{GemmKind::kWide, w.mt, w.ns, w.wn, false, splits > 1 ? (M <= 32 ? "w4_wide_32x128_splitk"
-                                                                                     : "w4_wide_64x128_splitk")
-                                                                        : w.name};
+      p = GemmPlan{GemmKind::kWide, w.mt, w.ns, w.wn, false, splits > 1 ? split_names[idx] : w.name};
       p.wide = idx;
       p.splits = splits;
       return p;
     }
     int pick = kNumWide - 1;
     for (int i = 0; i < kNumWide; ++i) {
+      if (i == 1 && T <= 1024) continue;  // 64x256 only on wide layers (64x128 measured faster below)
       const WideChoice& w = kWide[i];
       const int64_t bm = 16 * w.mt, bn = 16 * w.ns * w.wn;
       const int64_t wgs = ((s.N + bn - 1) / bn) * ((M + bm - 1) / bm);
-      if (M >= w.min_m && bm <= M && wgs >= 256) {
+      if (M >= w.min_m && (bm <= M || bm == 32) && wgs >= 256) {
         pick = i;
         break;
       }
