@@ -161,6 +161,35 @@ w4_status w4a16_linear(const w4_layer* layer, int64_t M, const void* x, const in
                        const void* tiled_scales, const int32_t* tiled_qzeros, const int32_t* perm,
                        const void* bias, void* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Grouped W4A16 linear for mixture-of-experts layers (the WNA16 MoE path of
+ * the vLLM AWQ practice page, section 5.4, and of the SGLang quantization
+ * page's MoE section): num_experts experts share one w4_layer description
+ * (K, N, group size, zero points, dtype; act-order is not supported and
+ * returns W4_ERR_UNSUPPORTED), each with its own tiled weights, and
+ *   y[r] = x[r] W_e (+ bias_e)   for every row r of expert e.
+ *   x              act [total_rows][K] row-major (device, 16-byte aligned):
+ *                  the rows routed to each expert, grouped by expert (the
+ *                  routing and the gather/scatter of tokens belong to the
+ *                  caller)
+ *   expert_offsets int32 [num_experts + 1] (device): expert e owns rows
+ *                  [expert_offsets[e], expert_offsets[e + 1]); nondecreasing,
+ *                  from 0 to total_rows.  Entries are clamped into
+ *                  [0, total_rows] (bad offsets give wrong rows, never an
+ *                  access outside x or y).
+ *   max_rows       host upper bound on the rows of any one expert (sizes the
+ *                  launch; rows of an expert beyond it are not computed), or
+ *                  0 for total_rows
+ *   tiled_qweight, tiled_scales, tiled_qzeros
+ *                  the num_experts per-expert buffers of w4_repack_gptq,
+ *                  each exactly w4_sizes() bytes, stacked in expert order
+ *   bias           act [num_experts][N] or NULL
+ *   y              act [total_rows][N] row-major (device) -- written
+ * Asynchronous on `stream`; no workspace.  Accuracy as for w4a16_linear. */
+w4_status w4a16_moe_linear(const w4_layer* layer, int32_t num_experts, int64_t total_rows, int64_t max_rows,
+                           const void* x, const int32_t* expert_offsets, const int32_t* tiled_qweight,
+                           const void* tiled_scales, const int32_t* tiled_qzeros, const void* bias, void* y,
+                           void* stream);
+
 /* Dense dequantization (the unfused path the fused GEMM is measured against).
  * The vLLM AWQ practice page (section 5.3) runs large batches as "dequantize,
  * then matmul" instead of the fused kernel; this call is the first half of

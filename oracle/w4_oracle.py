@@ -54,7 +54,7 @@ __all__ = [
     "pack_std", "unpack_std", "pack_std_zeros", "unpack_std_zeros", "std_zeros_transposed",
     "awq_to_std", "half_to_f64", "bf16_to_f64", "act_to_f64",
     "group_index", "dequant", "linear_ref", "codes_from_inputs", "reference_linear",
-    "reference_entries", "actorder_perm", "gidx_status", "GIDX_OUT_OF_RANGE", "GIDX_UNEQUAL_GROUPS",
+    "reference_entries", "reference_moe", "actorder_perm", "gidx_status", "GIDX_OUT_OF_RANGE", "GIDX_UNEQUAL_GROUPS",
     "tile_layout", "untile_codes",
     "TILE_N", "TILE_K", "TILE_SLOT_OF_OFFSET", "check",
 ]
@@ -282,6 +282,21 @@ def reference_entries(x, fmt, dtype, qweight, qzeros, scales, group_size, rows, 
 # ----------------------------------------------------------------------------
 # Act-order row order and g_idx validation
 # ----------------------------------------------------------------------------
+
+def reference_moe(x, offsets, fmt, dtype, experts, group_size, bias=None) -> np.ndarray:
+    """Grouped (mixture-of-experts) layer, float64 [total_rows, N]: rows
+    [offsets[e], offsets[e + 1]) of x go through expert e's linear layer
+    (experts: list of (qweight, qzeros, scales) checkpoint inputs; bias:
+    [E, N] or None).  The experts share K, N, format and group size (the WNA16
+    MoE path of [P2] 5.4); each expert is the plain layer of
+    ``reference_linear``."""
+    out = []
+    for e, (qw, qz, sc) in enumerate(experts):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        b = None if bias is None else bias[e]
+        out.append(reference_linear(np.asarray(x)[r0:r1], fmt, dtype, qw, qz, sc, group_size, bias=b))
+    return np.concatenate(out, axis=0)
+
 
 def actorder_perm(g_idx) -> np.ndarray:
     """Stable ascending sort of input rows by group (ties keep the original

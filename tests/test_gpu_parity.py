@@ -527,3 +527,52 @@ def test_linear_smallest_layers(W, dtype):
             y, guard = _run_linear(W, Lyr, x, bias, guard_rows=3)
             assert (guard.view(np.uint16) == 0x7F7F).all(), "write past row M"
             _assert_close(y, ref, dtype, f"smallest K={K} N={N} M={M}")
+
+
+# ----------------------------------------------------------------------------
+# Grouped (mixture-of-experts) layer
+# ----------------------------------------------------------------------------
+
+MOE_VARIANTS = [
+    # (name, fmt, group_size, has_zeros, dtype, with_bias)
+    ("awq-fp16-g128-bias", "awq", 128, True, "fp16", True),
+    ("std-bf16-g64-sym", "std", 64, False, "bf16", False),
+    ("std-fp16-g32-z", "std", 32, True, "fp16", False),
+]
+# rows per expert: empty experts, 1-row experts, ragged tiles, up to 130 rows
+MOE_ROWS = [[3, 0, 17, 1, 40, 0], [16, 16, 16, 16], [130, 0, 64, 33], [1, 1, 1, 1, 1, 1, 1, 1]]
+
+
+@pytest.mark.parametrize("v", MOE_VARIANTS, ids=[v[0] for v in MOE_VARIANTS])
+def test_moe_linear_matches_the_oracle(W, v):
+    import torch
+    name, fmt, gs, has_z, dtype, with_bias = v
+    K = 1152
+    G = K // gs
+    lo, hi = (0.002, 0.02) if dtype == "fp16" else (0.001, 0.01)
+    for N in (512, 4096):
+        for rows in MOE_ROWS:
+            E = len(rows)
+            experts = []
+            for e in range(E):
+                rng = seeded(707, K, N, e, len(name))
+                experts.append((random_words(rng, (K, N // 8) if fmt == "awq" else (K // 8, N)),
+                                random_words(rng, (G, N // 8)) if has_z else None,
+                                uniform_scales(rng, (G, N), lo, hi, dtype)))
+            moe = W.W4A16MoELinear(E, K, N, gs, has_z, dtype, fmt)
+            moe.process_weights_after_loading([(to_dev(q), to_dev(z) if z is not None else None, to_dev(s))
+                                               for q, z, s in experts])
+            offsets = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+            R = int(offsets[-1])
+            x = normal_acts(seeded(708, R, K, N), (R, K), dtype)
+            bias = uniform_scales(seeded(709, E, N), (E, N), -1.0, 1.0, dtype) if with_bias else None
+            ref = O.reference_moe(x, offsets, fmt, dtype, experts, gs, bias=bias)
+            for max_rows in (0, max(rows)):
+                say(f"moe {name} N={N} rows={rows} max_rows={max_rows}")
+                buf = filled((R + 2, N), act_dtype(dtype), 0x7F)
+                moe.apply(to_dev(x), to_dev(offsets), max_rows, to_dev(bias) if bias is not None else None,
+                          out=buf[:R])
+                _sync()
+                y = to_host(buf[:R])
+                assert (to_host(buf[R:]).view(np.uint16) == 0x7F7F).all(), "write past the last row"
+                _assert_close(y, ref, dtype, f"moe {name} N={N} rows={rows}")

@@ -415,6 +415,64 @@ def test_check_thresholds():
 
 
 # ----------------------------------------------------------------------------
+# Grouped (mixture-of-experts) reference
+# ----------------------------------------------------------------------------
+
+def _moe_experts(E, K, N, gs, seed):
+    out = []
+    for e in range(E):
+        rng = seeded(909, seed, e)
+        G = K // gs
+        out.append((random_words(rng, (K, N // 8)), random_words(rng, (G, N // 8)),
+                    uniform_scales(rng, (G, N), 0.002, 0.02, "fp16")))
+    return out
+
+
+def test_moe_closed_form_constant_experts():
+    # expert e with constant code c_e, zero z_e and scale s_e maps row r of its
+    # range to (c_e - z_e) s_e sum_k x[r, k] (+ its bias), whatever the others hold
+    K, N, gs = 256, 16, 128
+    G = K // gs
+    consts = [(13, 2, 0.0078125), (0, 15, 0.015625), (9, 9, 0.5)]
+    experts = [(constant_words((K, N // 8), c), constant_words((G, N // 8), z), np.full((G, N), s, np.float16))
+               for c, z, s in consts]
+    offsets = np.array([0, 2, 2, 5])          # the second expert owns no row
+    x = normal_acts(seeded(910), (5, K), "fp16")
+    bias = uniform_scales(seeded(911), (3, N), -1, 1, "fp16")
+    y = O.reference_moe(x, offsets, "awq", "fp16", experts, gs, bias=bias)
+    xs = x.astype(np.float64).sum(axis=1)
+    expect = np.empty((5, N))
+    for e, (c, z, s) in enumerate(consts):
+        for r in range(offsets[e], offsets[e + 1]):
+            expect[r] = (c - z) * s * xs[r] + bias[e].astype(np.float64)
+    np.testing.assert_allclose(y, expect, rtol=1e-13, atol=1e-13)
+
+
+def test_moe_one_expert_is_the_dense_layer_and_experts_are_independent():
+    K, N, gs = 256, 32, 128
+    experts = _moe_experts(3, K, N, gs, 1)
+    x = normal_acts(seeded(912), (7, K), "fp16")
+    # one expert owning every row == the plain layer
+    y1 = O.reference_moe(x, np.array([0, 7]), "awq", "fp16", experts[:1], gs)
+    qw, qz, sc = experts[0]
+    np.testing.assert_array_equal(y1, O.reference_linear(x, "awq", "fp16", qw, qz, sc, gs))
+    # reordering the experts together with their row ranges reorders the output rows
+    offs = np.array([0, 3, 4, 7])
+    y = O.reference_moe(x, offs, "awq", "fp16", experts, gs)
+    order = [2, 0, 1]
+    xr = np.concatenate([x[offs[e]:offs[e + 1]] for e in order])
+    offr = np.concatenate([[0], np.cumsum([offs[e + 1] - offs[e] for e in order])])
+    yr = O.reference_moe(xr, offr, "awq", "fp16", [experts[e] for e in order], gs)
+    np.testing.assert_array_equal(yr, np.concatenate([y[offs[e]:offs[e + 1]] for e in order]))
+    # an expert's rows do not depend on another expert's weights
+    other = _moe_experts(3, K, N, gs, 2)
+    y2 = O.reference_moe(x, offs, "awq", "fp16", [experts[0], other[1], experts[2]], gs)
+    np.testing.assert_array_equal(y2[:3], y[:3])
+    np.testing.assert_array_equal(y2[4:], y[4:])
+    assert not np.array_equal(y2[3:4], y[3:4])
+
+
+# ----------------------------------------------------------------------------
 # Mutation tests: plant a mistake in the oracle and show a pin catches it
 # ----------------------------------------------------------------------------
 

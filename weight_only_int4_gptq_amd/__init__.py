@@ -10,13 +10,13 @@ from ._abi import (  # noqa: F401
     W4Error, W4_OK, W4_ERR_INVALID_ARGUMENT, W4_ERR_UNSUPPORTED, W4_ERR_WORKSPACE, W4_ERR_HIP,
     W4_FP16, W4_BF16, w4_layer, w4_sizes_t, make_layer, lib,
     w4_check_layer, w4_sizes, w4_workspace_size, w4_kernel_name, w4_status_str,
-    w4_repack_awq, w4_repack_gptq, w4a16_linear, w4_dequant_dense,
+    w4_repack_awq, w4_repack_gptq, w4a16_linear, w4_dequant_dense, w4a16_moe_linear,
 )
 
 
 def __getattr__(name):
     # torch is imported lazily so that the host-only calls work without it
-    if name == "W4A16Linear":
-        from .layer import W4A16Linear
-        return W4A16Linear
+    if name in ("W4A16Linear", "W4A16MoELinear"):
+        from . import layer
+        return getattr(layer, name)
     raise AttributeError(name)

@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
             "w4_repack_gptq": ([P(w4_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP], ctypes.c_int),
             "w4a16_linear": ([P(w4_layer), I64, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
             "w4_dequant_dense": ([P(w4_layer), VP, VP, VP, VP, VP, VP], ctypes.c_int),
+            "w4a16_moe_linear": ([P(w4_layer), ctypes.c_int32, I64, I64, VP, VP, VP, VP, VP, VP, VP, VP],
+                                 ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -146,3 +148,11 @@ def w4_dequant_dense(layer, tiled_qweight, tiled_scales, tiled_qzeros, perm, w, 
     _raise("w4_dequant_dense", lib().w4_dequant_dense(
         ctypes.byref(layer), _ptr(tiled_qweight), _ptr(tiled_scales), _ptr(tiled_qzeros), _ptr(perm), _ptr(w),
         _stream(stream)))
+
+
+def w4a16_moe_linear(layer, num_experts, total_rows, max_rows, x, expert_offsets, tiled_qweight, tiled_scales,
+                     tiled_qzeros, bias, y, stream=None) -> None:
+    """Grouped W4A16 linear of a mixture-of-experts layer (rows grouped by expert)."""
+    _raise("w4a16_moe_linear", lib().w4a16_moe_linear(
+        ctypes.byref(layer), int(num_experts), int(total_rows), int(max_rows), _ptr(x), _ptr(expert_offsets),
+        _ptr(tiled_qweight), _ptr(tiled_scales), _ptr(tiled_qzeros), _ptr(bias), _ptr(y), _stream(stream)))

@@ -162,6 +162,31 @@ w4_status w4a16_linear(const w4_layer* L, int64_t M, const void* x, const int32_
   return W4_OK;
 }
 
+w4_status w4a16_moe_linear(const w4_layer* L, int32_t num_experts, int64_t total_rows, int64_t max_rows,
+                           const void* x, const int32_t* expert_offsets, const int32_t* tiled_qweight,
+                           const void* tiled_scales, const int32_t* tiled_qzeros, const void* bias, void* y,
+                           void* stream) {
+  w4_status st = w4_check_layer(L);
+  if (st != W4_OK) return st;
+  const Shape s = w4::shape_of(L);
+  if (s.has_perm) return W4_ERR_UNSUPPORTED;  // act-order experts are not supported
+  if (num_experts < 0 || total_rows < 0 || max_rows < 0) return W4_ERR_INVALID_ARGUMENT;
+  if (num_experts > 65535 || total_rows > kMaxM) return W4_ERR_UNSUPPORTED;
+  if (num_experts == 0 || total_rows == 0) return W4_OK;
+  if (max_rows == 0 || max_rows > total_rows) max_rows = total_rows;
+  if (!x || !expert_offsets || !tiled_qweight || !tiled_scales || !y) return W4_ERR_INVALID_ARGUMENT;
+  if (s.has_z != (tiled_qzeros != nullptr)) return W4_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(tiled_qweight, 16) || !aligned(tiled_scales, 2) || !aligned(y, 2) ||
+      !aligned(expert_offsets, 4) || (bias && !aligned(bias, 2)) || (tiled_qzeros && !aligned(tiled_qzeros, 4)))
+    return W4_ERR_INVALID_ARGUMENT;
+  st = device_status();
+  if (st != W4_OK) return st;
+  if (w4::launch_moe(s, num_experts, total_rows, max_rows, x, expert_offsets, tiled_qweight, tiled_scales,
+                     tiled_qzeros, bias, y, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return W4_ERR_HIP;
+  return W4_OK;
+}
+
 w4_status w4_dequant_dense(const w4_layer* L, const int32_t* tiled_qweight, const void* tiled_scales,
                            const int32_t* tiled_qzeros, const int32_t* perm, void* w, void* stream) {
   w4_status st = w4_check_layer(L);

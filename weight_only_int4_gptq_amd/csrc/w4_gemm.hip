@@ -532,7 +532,8 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
                                                           const uint32_t* __restrict__ zs,
                                                           const uint16_t* __restrict__ bias,
                                                           uint16_t* __restrict__ y, float* __restrict__ part,
-                                                          int64_t M, int64_t K, int64_t N, int G) {
+                                                          const int32_t* __restrict__ offs, int64_t M,
+                                                          int64_t K, int64_t N, int G) {
   using C = WideCfg<MT, NS, WN, S>;
   constexpr int NP = Groups<GM>::kPeriods, SP = Groups<GM>::kSteps;
   constexpr int NA = C::NA;
@@ -570,8 +571,29 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
   const int64_t nblk = K / kTileK;
   // split-K: workgroup z of gridDim.z walks blocks [kb0, kb0 + nb) (nb >= 1:
   // the host never splits finer than one block)
-  const int64_t kb0 = nblk * blockIdx.z / gridDim.z;
-  const int64_t nb = nblk * (blockIdx.z + 1) / gridDim.z - kb0;
+  int64_t split = blockIdx.z, nsplit = gridDim.z;
+  if (offs != nullptr) {
+    // grouped (mixture-of-experts) launch: workgroup z serves expert z, whose
+    // rows [offs[z], offs[z + 1]) of x and y are contiguous (clamped into the
+    // M rows given) and whose tiled weights, scales, zeros and bias follow
+    // those of the previous expert
+    const int64_t e = blockIdx.z;
+    int64_t r0 = offs[e], r1 = offs[e + 1];
+    r0 = r0 < 0 ? 0 : (r0 > M ? M : r0);
+    r1 = r1 < r0 ? r0 : (r1 > M ? M : r1);
+    M = r1 - r0;
+    if ((int64_t)blockIdx.y * C::BM >= M) return;  // uniform: the workgroup leaves before any barrier
+    x += r0 * K;
+    y += r0 * N;
+    qw += e * (K * N / 32);
+    sc += e * N * G;
+    if (HAS_Z) zs += e * (N / 8) * G;
+    if (bias != nullptr) bias += e * N;
+    split = 0;
+    nsplit = 1;
+  }
+  const int64_t kb0 = nblk * split / nsplit;
+  const int64_t nb = nblk * (split + 1) / nsplit - kb0;
   const int64_t m0 = (int64_t)blockIdx.y * C::BM;
   const int64_t tw0 = ((int64_t)blockIdx.x * WN + wave) * NS;  // first strip of this wave
   const uint32_t zshift = 4u * (uint32_t)(c & 7);
@@ -723,7 +745,7 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
   // epilogue: lane holds column c of each strip, rows 4 quad + r of each tile;
   // with split-K the fp32 partial goes to part[z][m][n] (bias and rounding
   // happen in split_reduce)
-  float* pz = part != nullptr ? part + (int64_t)blockIdx.z * M * N : nullptr;
+  float* pz = part != nullptr ? part + split * M * N : nullptr;
 #pragma unroll
   for (int nt = 0; nt < NS; ++nt) {
     const int64_t t = tw0 + nt;
@@ -798,6 +820,9 @@ struct Args {
   uint16_t* y;
   float* part;  // split-K partials [splits][M][N] (workspace), or nullptr
   int splits;   // K ranges (gridDim.z); 1 = no split
+  const int32_t* offs;  // grouped launch: expert row offsets [groups + 1], or nullptr
+  int groups;           // grouped launch: experts (gridDim.z)
+  int64_t max_rows;     // grouped launch: rows of the largest expert (grid height)
   int64_t M, K, N;
   int G, gs;
 };
@@ -858,11 +883,12 @@ hipError_t run_wide(const Args& a, const uint16_t* x, hipStream_t st) {
   using C = WideCfg<MT, NS, WN, S>;
   const int64_t T = a.N / kTileN;
   const int splits = a.splits > 1 ? a.splits : 1;
-  if (splits > 1 && (a.part == nullptr || splits > a.K / kTileK)) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((T + NS * WN - 1) / (NS * WN)), (unsigned)((a.M + C::BM - 1) / C::BM),
-                  (unsigned)splits);
+  if (splits > 1 && (a.part == nullptr || splits > a.K / kTileK || a.offs != nullptr)) return hipErrorInvalidValue;
+  const int64_t rows = a.offs != nullptr ? a.max_rows : a.M;
+  const dim3 grid((unsigned)((T + NS * WN - 1) / (NS * WN)), (unsigned)((rows + C::BM - 1) / C::BM),
+                  (unsigned)(a.offs != nullptr ? a.groups : splits));
   gemm_wide<MT, NS, WN, S, GM, BF16, HZ><<<grid, 64 * WN, 0, st>>>(
-      x, a.qw, a.sc, a.zs, a.bias, a.y, splits > 1 ? a.part : nullptr, a.M, a.K, a.N, a.G);
+      x, a.qw, a.sc, a.zs, a.bias, a.y, splits > 1 ? a.part : nullptr, a.offs, a.M, a.K, a.N, a.G);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int64_t total4 = a.M * a.N / 4;
@@ -1068,6 +1094,9 @@ hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* 
   a.y = static_cast<uint16_t*>(y);
   a.part = nullptr;
   a.splits = 1;
+  a.offs = nullptr;
+  a.groups = 0;
+  a.max_rows = M;
   a.M = M;
   a.K = s.K;
   a.N = s.N;
@@ -1088,6 +1117,56 @@ hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* 
   if (p.xl) return p.kw == 16 ? pick_flags<1, 1, 16, true>(sk, a, st) : pick_flags<1, 1, 8, true>(sk, a, st);
   if (p.nb == 2) return p.kw == 16 ? pick_flags<1, 2, 16, false>(sk, a, st) : pick_flags<1, 2, 8, false>(sk, a, st);
   return pick_flags<1, 1, 8, false>(sk, a, st);
+}
+
+GemmPlan plan_moe(const Shape& s, int64_t max_rows, int experts) {
+  // grouped launch of the wide kernel (no split-K): 16-row tiles for up to
+  // 16 rows per expert, else the largest tile not taller than the rows that
+  // still gives >= 256 workgroups over all experts
+  const int64_t T = s.N / kTileN;
+  int idx = kNumWide - 1;
+  if (max_rows <= 16) {
+    idx = T * experts >= 1024 ? kWide16x32 : kWide16x16;
+  } else {
+    for (int i = 0; i < kNumWide; ++i) {
+      const WideChoice& w = kWide[i];
+      const int64_t bm = 16 * w.mt, bn = 16 * w.ns * w.wn;
+      const int64_t wgs = ((s.N + bn - 1) / bn) * ((max_rows + bm - 1) / bm) * experts;
+      if (max_rows >= w.min_m && (bm <= max_rows || bm == 32) && wgs >= 256) {
+        idx = i;
+        break;
+      }
+    }
+  }
+  const WideChoice& w = kWide[idx];
+  GemmPlan p{GemmKind::kWide, w.mt, w.ns, w.wn, false, w.name};
+  p.wide = idx;
+  return p;
+}
+
+hipError_t launch_moe(const Shape& s, int experts, int64_t total_rows, int64_t max_rows, const void* x,
+                      const int32_t* offsets, const int32_t* tiled_w, const void* tiled_s, const int32_t* tiled_z,
+                      const void* bias, void* y, hipStream_t st) {
+  Args a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.qw = reinterpret_cast<const u4*>(tiled_w);
+  a.sc = static_cast<const uint16_t*>(tiled_s);
+  a.zs = reinterpret_cast<const uint32_t*>(tiled_z);
+  a.perm = nullptr;
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.y = static_cast<uint16_t*>(y);
+  a.part = nullptr;
+  a.splits = 1;
+  a.offs = offsets;
+  a.groups = experts;
+  a.max_rows = max_rows;
+  a.M = total_rows;
+  a.K = s.K;
+  a.N = s.N;
+  a.G = s.G;
+  a.gs = s.gs;
+  const GemmPlan p = plan_moe(s, max_rows, experts);
+  return wide_dispatch(p.wide, s, a, a.x, st);
 }
 
 }  // namespace w4

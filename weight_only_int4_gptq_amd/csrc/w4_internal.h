@@ -65,6 +65,12 @@ hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* 
                        const int32_t* tiled_z, const int32_t* perm, const void* bias, void* y, void* ws,
                        hipStream_t st);
 
+// ---- grouped (mixture-of-experts) GEMM (w4_gemm.hip) ----
+GemmPlan plan_moe(const Shape& s, int64_t max_rows, int experts);
+hipError_t launch_moe(const Shape& s, int experts, int64_t total_rows, int64_t max_rows, const void* x,
+                      const int32_t* offsets, const int32_t* tiled_w, const void* tiled_s, const int32_t* tiled_z,
+                      const void* bias, void* y, hipStream_t st);
+
 // ---- dense dequantization, the unfused comparison path (w4_dequant.hip) ----
 hipError_t launch_dequant_dense(const Shape& s, const int32_t* tiled_w, const void* tiled_s, const int32_t* tiled_z,
                                 const int32_t* perm, void* w, hipStream_t st);

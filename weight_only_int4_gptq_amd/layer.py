@@ -122,3 +122,41 @@ class W4A16Linear:
 
     def kernel_name(self, M: int) -> str:
         return A.w4_kernel_name(self.layer, M)
+
+
+class W4A16MoELinear:
+    """The grouped (mixture-of-experts) layer: E experts of one shape, each
+    repacked into its slice of stacked tile buffers, applied in one launch to
+    rows grouped by expert (w4a16_moe_linear).  Act-order is not supported."""
+
+    def __init__(self, num_experts: int, K: int, N: int, group_size: int = 128, has_zero_points: bool = True,
+                 dtype: str = "fp16", fmt: str = "awq", device="cuda"):
+        self.E = int(num_experts)
+        self.experts = [W4A16Linear(K, N, group_size, has_zero_points, False, dtype, fmt, device=device)
+                        for _ in range(self.E)]
+        self.K, self.N, self.dtype = K, N, dtype
+        self.layer = self.experts[0].layer
+        self.tiled = None
+
+    def process_weights_after_loading(self, weights, stream=None) -> dict:
+        """weights: per expert (qweight, qzeros, scales) as loaded."""
+        tiled = [ex.process_weights_after_loading(qw, qz, sc, None, stream) for ex, (qw, qz, sc) in
+                 zip(self.experts, weights)]
+        self.tiled = {k: (torch.stack([t[k] for t in tiled]).contiguous() if tiled[0][k] is not None else None)
+                      for k in ("qweight", "scales", "qzeros")}
+        for ex in self.experts:
+            ex.tiled = None  # the stacked copy is the one kept
+        return self.tiled
+
+    def apply(self, x: torch.Tensor, expert_offsets: torch.Tensor, max_rows: int = 0, bias=None, out=None,
+              stream=None) -> torch.Tensor:
+        """y [R, N] for rows x [R, K] grouped by expert (expert_offsets int32 [E + 1] on the device)."""
+        if self.tiled is None:
+            raise RuntimeError("process_weights_after_loading has not run")
+        x2 = x.contiguous()
+        R = x2.shape[0]
+        y = out if out is not None else torch.empty((R, self.N), dtype=x.dtype, device=x.device)
+        t = self.tiled
+        A.w4a16_moe_linear(self.layer, self.E, R, max_rows, x2, expert_offsets, t["qweight"], t["scales"],
+                           t["qzeros"], bias, y, stream)
+        return y
