@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", default="decode", choices=["tiny", "decode", "mid", "prefill", "actorder"])
+    p.add_argument("--config", default="decode", choices=["tiny", "decode", "mid", "prefill", "actorder", "moe"])
     p.add_argument("--reps", type=int, default=0, help="launches per case for the per-kernel timing (0 = auto)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -112,6 +112,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     W.lib()
+    if args.config == "moe":
+        return main_moe(args, torch, W)
     cfg_id = {"tiny": 1, "decode": 2, "mid": 3, "prefill": 4, "actorder": 5}[args.config]
     cases = [c for c in CONFIGS if c.cfg_id == cfg_id]
     if args.group_size:
@@ -290,6 +292,126 @@ def main():
         "cpu_baseline": cpu,
         "per_case": per_case,
         "repack": repack,
+    }
+    print(json.dumps(out), flush=True)
+
+
+# Mixture-of-experts workload (not one of the five layer workloads): the fused
+# gate/up projection of a Mixtral-8x7B-class MoE layer, 8 experts of
+# (K, N) = (4096, 28672), fp16 AWQ g = 128 with zero points, tokens routed
+# top-2 by a seeded random router; rows per step 32 (16 decode tokens),
+# 512 (256 tokens) and 4096 (2048 prefill tokens).
+MOE_E, MOE_K, MOE_N, MOE_TOKENS, MOE_TOPK = 8, 4096, 28672, (16, 256, 2048), 2
+
+
+def main_moe(args, torch, W):
+    from synthetic import normal_acts, random_words, seeded, uniform_scales
+    stream = torch.cuda.current_stream()
+    E, K, N = MOE_E, MOE_K, MOE_N
+    G = K // 128
+    experts = []
+    for e in range(E):
+        rng = seeded(6, K, N, e)
+        experts.append((random_words(rng, (K, N // 8)), random_words(rng, (G, N // 8)),
+                        uniform_scales(rng, (G, N), 0.002, 0.02, "fp16")))
+    moe = W.W4A16MoELinear(E, K, N, 128, True, "fp16", "awq")
+    moe.process_weights_after_loading([tuple(_to_dev(torch, a) for a in ex) for ex in experts])
+    t0 = moe.tiled
+    per_set = sum(v.numel() * v.element_size() for v in t0.values() if v is not None)
+    R = max(2, math.ceil(ROTATE_BYTES / per_set))
+    sets = [t0] + [{k: (v.clone() if v is not None else None) for k, v in t0.items()} for _ in range(R - 1)]
+    runs = []
+    for T in MOE_TOKENS:
+        rng = seeded(7, T)
+        choice = np.stack([rng.choice(E, size=MOE_TOPK, replace=False) for _ in range(T)])  # top-2 experts
+        counts = np.bincount(choice.reshape(-1), minlength=E)
+        offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        rows = int(offs[-1])
+        x = _to_dev(torch, normal_acts(seeded(8, rows, K), (rows, K), "fp16"))
+        y = torch.empty((rows, N), dtype=torch.float16, device="cuda")
+        runs.append(dict(T=T, rows=rows, max_rows=int(counts.max()), offs=_to_dev(torch, offs), x=x, y=y,
+                         counts=counts.tolist(), i=0))
+
+    def launch(r):
+        t = sets[r["i"] % len(sets)]
+        r["i"] += 1
+        W.w4a16_moe_linear(moe.layer, E, r["rows"], r["max_rows"], r["x"], r["offs"], t["qweight"], t["scales"],
+                           t["qzeros"], None, r["y"], torch.cuda.current_stream())
+
+    def timed(fn, count):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(count)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    wbytes = E * K * N // 2
+    per_case = []
+    for r in runs:
+        for _ in range(3):
+            launch(r)
+        torch.cuda.synchronize()
+        reps = 20 if r["rows"] >= 1024 else 60
+        us = timed(lambda n: [launch(r) for _ in range(n)], reps) * 1e3 / reps
+        tb = wbytes + E * G * N * 2 + E * G * N // 2 + r["rows"] * (K + N) * 2
+        fl = 2.0 * r["rows"] * K * N
+        per_case.append(dict(tokens=r["T"], rows=r["rows"], rows_per_expert=r["counts"], us=round(us, 3),
+                             weight_GBps=round(wbytes / (us * 1e-6) / 1e9, 1), TFLOPS=round(fl / (us * 1e-6) / 1e12, 2),
+                             _tb=tb, _fl=fl, _us=us))
+
+    def step():
+        for r in runs:
+            launch(r)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0w = time.perf_counter()
+    ms_step = timed(lambda n: [step() for _ in range(n)], args.steps) / args.steps
+    wall = time.perf_counter() - t0w
+    value = len(runs) * wbytes / (ms_step * 1e-3) / 1e9
+    sum_tb = sum(p["_tb"] for p in per_case)
+    sum_fl = sum(p["_fl"] for p in per_case)
+    sum_us = sum(p["_us"] for p in per_case)
+    if sum_fl / sum_tb < (MFMA_F16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9):
+        ach = sum_tb / (sum_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        ach = sum_fl / (sum_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = ["w4a16_moe_linear (wide kernel, grouped)"]
+    roof["avg_launch_us"] = round(sum_us / len(per_case), 3)
+    cpu = None
+    if not args.no_cpu:
+        import oracle as O
+        qw, qz, sc = experts[0]
+        xs = normal_acts(seeded(9, 4, K), (4, K), "fp16")
+        tc = time.perf_counter()
+        O.reference_moe(xs, np.array([0, 4]), "awq", "fp16", [experts[0]], 128)
+        dt = time.perf_counter() - tc
+        cpu = {"value": round((K * N // 2) / dt / 1e9, 4), "unit": "GB/s", "cores": os.cpu_count(), "kind": "oracle",
+               "sample": "one expert (K=4096, N=28672) on 4 rows", "seconds": round(dt, 2)}
+    for p in per_case:
+        for k in ("_tb", "_fl", "_us"):
+            p.pop(k)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded uniform int4 codes/zeros, uniform scales, N(0,1) activations, random top-2 routing)",
+        "config": {"workload": f"moe: E={E} experts of (K={K},N={N}) AWQ g=128 zeros, top-{MOE_TOPK} routing of "
+                               f"{list(MOE_TOKENS)} tokens", "cases": len(runs), "act_dtype": "fp16",
+                   "weight_rotation_MiB": ROTATE_BYTES >> 20},
+        "timing": "HIP graph of the timed launches (one untimed replay uploads it, one replay is timed)",
+        "wall_s_timed": round(wall, 3), "roofline": roof, "cpu_baseline": cpu, "per_case": per_case,
     }
     print(json.dumps(out), flush=True)
 
