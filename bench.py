@@ -469,17 +469,20 @@ def cpu_baseline(cases, seconds):
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
     done, wbytes, spent = [], 0, 0.0
-    for c in cases:
-        Lw = make_layer_inputs(c)
-        for M in c.Ms:
-            x = make_acts(c, M)
-            t0 = time.perf_counter()
-            O.reference_linear(x, c.fmt, c.dtype, Lw["qweight"], Lw["qzeros"], Lw["scales"], c.group_size,
-                               g_idx=Lw["g_idx"])
-            dt = time.perf_counter() - t0
-            spent += dt
-            wbytes += c.K * c.N // 2
-            done.append(f"(K={c.K},N={c.N},M={M})")
+    for _ in range(8):  # passes over the workload until `seconds` of CPU time are spent
+        for c in cases:
+            Lw = make_layer_inputs(c)
+            for M in c.Ms:
+                x = make_acts(c, M)
+                t0 = time.perf_counter()
+                O.reference_linear(x, c.fmt, c.dtype, Lw["qweight"], Lw["qzeros"], Lw["scales"], c.group_size,
+                                   g_idx=Lw["g_idx"])
+                dt = time.perf_counter() - t0
+                spent += dt
+                wbytes += c.K * c.N // 2
+                done.append(f"(K={c.K},N={c.N},M={M})")
+                if spent >= seconds:
+                    break
             if spent >= seconds:
                 break
         if spent >= seconds:

@@ -84,7 +84,8 @@ w4_status w4_check_layer(const w4_layer* layer);
 w4_status w4_sizes(const w4_layer* layer, w4_sizes_t* out);
 
 /* Bytes of scratch device memory w4a16_linear needs for M rows (0 when the
- * chosen kernel needs none).  Host only. */
+ * chosen kernel needs none: M <= 16 without act-order, M > 256, or layers
+ * with N > 16384 and no act-order).  Host only. */
 w4_status w4_workspace_size(const w4_layer* layer, int64_t M, size_t* bytes);
 
 /* Name of the kernel w4a16_linear launches for M rows (the analogue of the
@@ -153,8 +154,10 @@ w4_status w4_repack_gptq(const w4_layer* layer, const int32_t* std_qweight, cons
  *   workspace      device scratch of >= w4_workspace_size() bytes (16-byte
  *                  aligned), or NULL when that size is 0; no initialization
  *                  needed.  With act-order it receives x with its columns
- *                  gathered through perm.  Calls that overlap in time must
- *                  not share a workspace.
+ *                  gathered through perm; for 16 < M <= 256 on layers with
+ *                  N <= 16384 it also holds the fp32 split-K partials
+ *                  [splits][M][N].  Calls that overlap in time must not
+ *                  share a workspace.
  * Accuracy: within max|y - ref| <= 1e-2 (1 + |ref|) elementwise and
  * relative Frobenius error <= 2e-3 of the float64 reference. */
 w4_status w4a16_linear(const w4_layer* layer, int64_t M, const void* x, const int32_t* tiled_qweight,

@@ -97,6 +97,7 @@ def test_linear_rejects_bad_arguments_before_any_launch(W):
     assert _lin(W, L, -1) == W.W4_ERR_INVALID_ARGUMENT
     assert _lin(W, L, 1, x=None) == W.W4_ERR_INVALID_ARGUMENT
     assert _lin(W, L, 1, y=None) == W.W4_ERR_INVALID_ARGUMENT
+    assert _lin(W, L, 1, y=18) == W.W4_ERR_INVALID_ARGUMENT              # y must be 4-byte aligned
     assert _lin(W, L, 1, qz=None) == W.W4_ERR_INVALID_ARGUMENT          # zero points declared, none given
     assert _lin(W, L, 1, x=24) == W.W4_ERR_INVALID_ARGUMENT             # x not 16-byte aligned
     assert _lin(W, L, 1, qw=8) == W.W4_ERR_INVALID_ARGUMENT

@@ -147,7 +147,7 @@ w4_status w4a16_linear(const w4_layer* L, int64_t M, const void* x, const int32_
   const Shape s = w4::shape_of(L);
   if (!x || !tiled_qweight || !tiled_scales || !y) return W4_ERR_INVALID_ARGUMENT;
   if (s.has_z != (tiled_qzeros != nullptr) || s.has_perm != (perm != nullptr)) return W4_ERR_INVALID_ARGUMENT;
-  if (!aligned(x, 16) || !aligned(tiled_qweight, 16) || !aligned(tiled_scales, 2) || !aligned(y, 2) ||
+  if (!aligned(x, 16) || !aligned(tiled_qweight, 16) || !aligned(tiled_scales, 2) || !aligned(y, 4) ||
       (bias && !aligned(bias, 2)) || (tiled_qzeros && !aligned(tiled_qzeros, 4)) || (perm && !aligned(perm, 16)))
     return W4_ERR_INVALID_ARGUMENT;
   if (M == 0) return W4_OK;

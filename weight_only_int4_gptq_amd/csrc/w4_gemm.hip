@@ -793,7 +793,9 @@ __global__ void split_reduce(const float* __restrict__ part, const uint16_t* __r
     }
     const uint32_t lo = (uint32_t)f32_to_act<BF16>(a.x) | ((uint32_t)f32_to_act<BF16>(a.y) << 16);
     const uint32_t hi = (uint32_t)f32_to_act<BF16>(a.z) | ((uint32_t)f32_to_act<BF16>(a.w) << 16);
-    reinterpret_cast<uint2*>(y)[idx] = make_uint2(lo, hi);
+    uint32_t* y32 = reinterpret_cast<uint32_t*>(y) + 2 * idx;  // y is 4-byte aligned
+    y32[0] = lo;
+    y32[1] = hi;
   }
 }
 
