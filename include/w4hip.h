@@ -62,9 +62,11 @@ typedef struct {
   size_t qzeros;        /* int32 [G][N/8]   AWQ or standard zero words (0 if none) */
   size_t scales;        /* act   [G][N]     scales as loaded                       */
   size_t std_qweight;   /* int32 [K/8][N]   standard qweight (packed along K)      */
-  size_t tiled_qweight; /* int32 K*N/8      tile layout (see w4_repack_gptq)       */
-  size_t tiled_scales;  /* act   [N/16][G][16]                                      */
-  size_t tiled_qzeros;  /* int32 [N/16][G][2] (0 if no zero points)                */
+  size_t tiled_qweight; /* int32 K*Np/8     tile layout (see w4_repack_gptq)       */
+  size_t tiled_scales;  /* act   [Np/16][G][16]                                     */
+  size_t tiled_qzeros;  /* int32 [Np/16][G][2] (0 if no zero points)               */
+  /* Np = N rounded up to a multiple of 16 (the tile layout pads a last half
+   * strip when N % 16 == 8) */
   size_t perm;          /* int32 [K] act-order row permutation (0 without g_idx)   */
 } w4_sizes_t;
 
@@ -73,7 +75,7 @@ typedef struct {
  *   W4_ERR_INVALID_ARGUMENT  layer == NULL, K <= 0, N <= 0;
  *   W4_ERR_UNSUPPORTED       group_size not in {-1, 32, 64, 128} (the group
  *                            sizes listed in section 5.3 of the vLLM AWQ
- *                            practice page), K % 128 != 0, N % 16 != 0,
+ *                            practice page), K % 128 != 0, N % 8 != 0,
  *                            K % group_size != 0, act_dtype not fp16/bf16,
  *                            has_g_idx with group_size == -1, K > 2^20 or
  *                            N > 2^20.
@@ -120,8 +122,8 @@ w4_status w4_repack_awq(const w4_layer* layer, const int32_t* awq_qweight, const
  *   scales         act   [G][N]        (device)
  *   g_idx          int32 [K]           (device; NULL iff !has_g_idx)
  *   tiled_qweight  int32 [K*N/8]       (device, 16-byte aligned) -- written
- *   tiled_scales   act   [N/16][G][16] (device) -- written
- *   tiled_qzeros   int32 [N/16][G][2]  (device; NULL iff !has_zero_points) -- written
+ *   tiled_scales   act   [Np/16][G][16] (device) -- written
+ *   tiled_qzeros   int32 [Np/16][G][2]  (device; NULL iff !has_zero_points) -- written
  *   perm           int32 [K]           (device; NULL iff !has_g_idx) -- written
  *   status_dev     int32 [1]           (device; may be NULL) -- written:
  *                  bit 0 = a g_idx entry outside [0, G); bit 1 = some group
@@ -132,9 +134,11 @@ w4_status w4_repack_awq(const w4_layer* layer, const int32_t* awq_qweight, const
  * (perm[k'] = original row of sorted row k'); a scale equal to zero is
  * replaced by the previous group's stored scale (1.0 for group 0) and the
  * codes of that group and column by its zero point; word [t][b][l][j]
- * (t < N/16, b < K/128, l < 64, j < 4) holds column 16t + l%16 at sorted
+ * (t < Np/16, b < K/128, l < 64, j < 4) holds column 16t + l%16 at sorted
  * rows 128b + 32j + 8(l/16) + e, e = 0..7, K-offset e in nibble slot
- * [0,4,1,5,2,6,3,7][e]. */
+ * [0,4,1,5,2,6,3,7][e].  Columns N .. Np-1 (a padded half strip) hold codes
+ * and zero points 8 and scale 1: their weights are 0 and no output column
+ * is written for them. */
 w4_status w4_repack_gptq(const w4_layer* layer, const int32_t* std_qweight, const int32_t* std_qzeros,
                          const void* scales, const int32_t* g_idx, int32_t* tiled_qweight,
                          void* tiled_scales, int32_t* tiled_qzeros, int32_t* perm, int32_t* status_dev,

@@ -339,8 +339,12 @@ def _one_bits(dtype: str) -> int:
 def tile_layout(std_qweight, std_qzeros, scales, group_size: int, dtype: str, g_idx=None) -> dict:
     """Repack standard weights into the tile layout consumed by the kernels.
 
-    Definition (K % 128 == 0, N % 16 == 0, g = K when group_size == -1,
-    G = K / g, every act-order group owning exactly g rows):
+    Definition (K % 128 == 0, N % 8 == 0, g = K when group_size == -1,
+    G = K / g, every act-order group owning exactly g rows).  The column
+    count is padded to Np = 16 ceil(N / 16) (the pages' tile padding, read
+    as: a padded column has every code and its zero point equal to 8 and
+    every scale equal to 1, so its weights are exactly 0); steps 3-5 then
+    run over Np columns:
 
     1. Row order: perm = stable argsort of g_idx (identity without g_idx);
        sorted row k' holds original row perm[k'] and lies in group k' // g.
@@ -361,7 +365,7 @@ def tile_layout(std_qweight, std_qzeros, scales, group_size: int, dtype: str, g_
     """
     q = unpack_std(std_qweight)
     K, N = q.shape
-    assert K % TILE_K == 0 and N % TILE_N == 0
+    assert K % TILE_K == 0 and N % 8 == 0
     gs = K if group_size == -1 else group_size
     G = K // gs
     z = None if std_qzeros is None else unpack_std_zeros(std_qzeros)
@@ -386,6 +390,15 @@ def tile_layout(std_qweight, std_qzeros, scales, group_size: int, dtype: str, g_
     zfull = np.full((G, N), 8, dtype=np.int64) if z is None else z
     rows_group = np.arange(K) // gs
     q = np.where(is_zero[rows_group, :], zfull[rows_group, :], q)
+
+    # Padding to Np columns: codes and zero points 8, scales 1.
+    Np = -(-N // TILE_N) * TILE_N
+    if Np != N:
+        q = np.concatenate([q, np.full((K, Np - N), 8, dtype=np.int64)], axis=1)
+        stored = np.concatenate([stored, np.full((G, Np - N), _one_bits(dtype), dtype=np.int64)], axis=1)
+        if z is not None:
+            z = np.concatenate([z, np.full((G, Np - N), 8, dtype=np.int64)], axis=1)
+    N = Np
 
     # Step 3: words [t, b, l, j] built from explicit index arithmetic.
     T, B = N // TILE_N, K // TILE_K

@@ -79,6 +79,9 @@ REPACK_VARIANTS = [
     ("fp16-g64-z-zeroscales", 384, 48, 64, True, False, "fp16", True),
     ("bf16-g128-sym-zeroscales-act", 512, 32, 128, False, True, "bf16", True),
     ("fp16-g128-z-act-8192", 8192, 256, 128, True, True, "fp16", False),
+    # N % 16 == 8: the last strip is half padding
+    ("fp16-g128-z-n264", 384, 264, 128, True, False, "fp16", False),
+    ("bf16-g64-sym-act-n40", 512, 40, 64, False, True, "bf16", True),
 ]
 
 
@@ -111,10 +114,11 @@ def test_repack_gptq_bit_exact(W, v):
     ref = O.tile_layout(sw, sz, s, gs, dtype, g_idx=gi)
     L = W.make_layer(K, N, gs, has_z, has_g, dtype)
     outs = []
+    T = (N + 15) // 16
     for fill in (0x00, 0xFF):
-        tw = filled((K * N // 8,), torch.int32, fill)
-        ts = filled((N // 16, G, 16), act_dtype(dtype), fill)
-        tz = filled((N // 16, G, 2), torch.int32, fill) if has_z else None
+        tw = filled((K * T * 2,), torch.int32, fill)
+        ts = filled((T, G, 16), act_dtype(dtype), fill)
+        tz = filled((T, G, 2), torch.int32, fill) if has_z else None
         pm = filled((K,), torch.int32, fill) if has_g else None
         st = filled((1,), torch.int32, fill)
         W.w4_repack_gptq(L, to_dev(sw), to_dev(sz) if has_z else None, to_dev(s), to_dev(gi) if has_g else None,
@@ -233,6 +237,10 @@ LINEAR_VARIANTS = [
     ("std-fp16-ch-z", "std", 384, 272, -1, True, False, "fp16", False),
     ("std-bf16-ch-sym", "std", 384, 272, -1, False, False, "bf16", False),
     ("std-bf16-g64-sym-act", "std", 512, 272, 64, False, True, "bf16", True),
+    # N % 16 == 8 (a padded half strip)
+    ("awq-fp16-g128-n264-bias", "awq", 384, 264, 128, True, False, "fp16", True),
+    ("std-bf16-g32-z-n40", "std", 512, 40, 32, True, False, "bf16", False),
+    ("std-fp16-g128-z-act-n24", "std", 512, 24, 128, True, True, "fp16", True),
 ]
 LINEAR_MS = (1, 3, 16, 17, 33, 64, 70, 130)
 
@@ -378,7 +386,7 @@ def test_linear_full_size_sampled(W, c, M):
 # K = 1152 is nine 128-row blocks, so every pipeline depth runs full trips and
 # a partial tail, and a 4-way split gives uneven K ranges (2, 2, 2, 3).
 WIDE_TILE_SHAPES = [(1024, 16384), (256, 32768), (64, 32768), (32, 32768), (40, 8192), (24, 8192), (200, 8192),
-                    (16, 12288), (9, 20480)]
+                    (16, 12288), (9, 20480), (300, 4104), (16, 16392)]
 WIDE_VARIANTS = [
     # (name, fmt, group_size, has_zeros, has_gidx, dtype)
     ("awq-fp16-g128", "awq", 128, True, False, "fp16"),
@@ -550,7 +558,7 @@ def test_moe_linear_matches_the_oracle(W, v):
     K = 1152
     G = K // gs
     lo, hi = (0.002, 0.02) if dtype == "fp16" else (0.001, 0.01)
-    for N in (512, 4096):
+    for N in (512, 4096, 136):
         for rows in MOE_ROWS:
             E = len(rows)
             experts = []

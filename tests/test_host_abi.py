@@ -50,7 +50,7 @@ def test_check_layer_status_codes(W):
         (dict(K=0), W.W4_ERR_INVALID_ARGUMENT), (dict(N=-16), W.W4_ERR_INVALID_ARGUMENT),
         (dict(group_size=16), W.W4_ERR_UNSUPPORTED), (dict(group_size=256), W.W4_ERR_UNSUPPORTED),
         (dict(group_size=0), W.W4_ERR_UNSUPPORTED), (dict(K=200), W.W4_ERR_UNSUPPORTED),
-        (dict(N=24), W.W4_ERR_UNSUPPORTED), (dict(K=2 ** 21), W.W4_ERR_UNSUPPORTED),
+        (dict(N=20), W.W4_ERR_UNSUPPORTED), (dict(K=2 ** 21), W.W4_ERR_UNSUPPORTED),
         (dict(group_size=-1, has_g_idx=True), W.W4_ERR_UNSUPPORTED), (dict(dtype=2), W.W4_ERR_UNSUPPORTED),
     ]
     for over, expect in bad:
@@ -59,6 +59,11 @@ def test_check_layer_status_codes(W):
         assert W.w4_check_layer(W.make_layer(**kw)) == expect, over
     for gs in (-1, 32, 64, 128):
         assert W.w4_check_layer(W.make_layer(384, 48, gs, False, False, "bf16")) == W.W4_OK
+    # N % 16 == 8 is accepted: the tile layout pads the last strip to 16 columns
+    assert W.w4_check_layer(W.make_layer(512, 24)) == W.W4_OK
+    s = W.w4_sizes(W.make_layer(512, 24, 128, True, False, "fp16"))
+    assert s["tiled_qweight"] == 512 * 32 // 2 and s["tiled_scales"] == 4 * 32 * 2
+    assert s["tiled_qzeros"] == 2 * 4 * 2 * 4 and s["std_qweight"] == 64 * 24 * 4
 
 
 def test_sizes_of_the_tiny_layer(W):

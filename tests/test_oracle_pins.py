@@ -414,6 +414,38 @@ def test_check_thresholds():
     assert not O.check(y, ref)["ok"]
 
 
+def test_tile_layout_pads_columns_to_whole_strips():
+    # N = 24: one full strip and one half strip; the padded columns hold
+    # codes and zero points 8 and scale 1 (weights exactly 0), the real
+    # columns are untouched
+    K, N, gs = 256, 24, 128
+    G = K // gs
+    rng = seeded(920)
+    sw = random_words(rng, (K // 8, N))
+    sz = random_words(rng, (G, N // 8))
+    sc = uniform_scales(rng, (G, N), 0.002, 0.02, "fp16")
+    t = O.tile_layout(sw, sz, sc, gs, "fp16")
+    assert t["qweight"].size == K * 32 // 8 and t["scales"].shape == (2, G, 16) and t["zeros"].shape == (2, G, 2)
+    full = O.untile_codes(t["qweight"], K, 32)
+    np.testing.assert_array_equal(full[:, :N], O.unpack_std(sw))
+    assert (full[:, N:] == 8).all()
+    assert (t["scales"][1, :, 8:] == 0x3C00).all()
+    np.testing.assert_array_equal(t["scales"][:, :, :].transpose(1, 0, 2).reshape(G, 32)[:, :N],
+                                  sc.view(np.uint16))
+    zw = O.u32(t["zeros"])
+    assert (zw[1, :, 1] == 0x88888888).all()
+    np.testing.assert_array_equal(zw[:, :, :].transpose(1, 0, 2).reshape(G, 4)[:, :3], O.u32(sz))
+    # the padded layer computes the same outputs as the unpadded definition
+    q, z = O.codes_from_inputs("std", sw, sz)
+    W = O.dequant(q, z, O.half_to_f64(sc), O.group_index(K, gs))
+    qp = full
+    zp = np.concatenate([z, np.full((G, 8), 8)], axis=1)
+    sp = np.concatenate([O.half_to_f64(sc), np.ones((G, 8))], axis=1)
+    Wp = O.dequant(qp, zp, sp, O.group_index(K, gs))
+    np.testing.assert_array_equal(Wp[:, :N], W)
+    assert (Wp[:, N:] == 0).all()
+
+
 # ----------------------------------------------------------------------------
 # Grouped (mixture-of-experts) reference
 # ----------------------------------------------------------------------------

@@ -44,7 +44,7 @@ w4_status w4_check_layer(const w4_layer* L) {
   const int gs = L->group_size;
   if (gs != -1 && gs != 32 && gs != 64 && gs != 128) return W4_ERR_UNSUPPORTED;
   if (L->K > kMaxDim || L->N > kMaxDim) return W4_ERR_UNSUPPORTED;
-  if (L->K % w4::kTileK != 0 || L->N % w4::kTileN != 0) return W4_ERR_UNSUPPORTED;
+  if (L->K % w4::kTileK != 0 || L->N % 8 != 0) return W4_ERR_UNSUPPORTED;  // N tail: padded strip
   if (gs != -1 && L->K % gs != 0) return W4_ERR_UNSUPPORTED;
   if (L->has_g_idx && gs == -1) return W4_ERR_UNSUPPORTED;
   return W4_OK;
@@ -60,9 +60,10 @@ w4_status w4_sizes(const w4_layer* L, w4_sizes_t* out) {
   out->qzeros = s.has_z ? G * (N / 8) * 4 : 0;
   out->scales = G * N * 2;
   out->std_qweight = (K / 8) * N * 4;
-  out->tiled_qweight = K * N / 2;
-  out->tiled_scales = G * N * 2;
-  out->tiled_qzeros = s.has_z ? (N / w4::kTileN) * G * 2 * 4 : 0;
+  const size_t Np = (size_t)s.Np;
+  out->tiled_qweight = K * Np / 2;
+  out->tiled_scales = G * Np * 2;
+  out->tiled_qzeros = s.has_z ? (Np / w4::kTileN) * G * 2 * 4 : 0;
   out->perm = s.has_perm ? K * 4 : 0;
   return W4_OK;
 }

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void dequant_dense_kernel(const uint4* __restr
                                                               uint16_t* __restrict__ w, int64_t K, int64_t N,
                                                               int G, int gs) {
   const int64_t nblk = K / kTileK;
-  const int64_t total = (N / kTileN) * nblk * 64;
+  const int64_t total = ((N + kTileN - 1) / kTileN) * nblk * 64;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int lane = (int)(idx & 63);
@@ -52,6 +52,7 @@ __global__ __launch_bounds__(256) void dequant_dense_kernel(const uint4* __restr
     const int64_t t = blk / nblk, b = blk - t * nblk;
     const int c = lane & 15, quad = lane >> 4;
     const int64_t n = t * kTileN + c;
+    if (n >= N) continue;  // the padded half of the last strip
     const uint4 v = tw[idx];
     const uint32_t words[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void dequant_dense_kernel(const uint4* __restr
 template <bool BF16, bool HZ>
 hipError_t launch_dq(const Shape& s, const uint4* tw, const uint16_t* ts, const uint32_t* tz, const int32_t* perm,
                      uint16_t* w, hipStream_t st) {
-  const int64_t total = (s.N / kTileN) * (s.K / kTileK) * 64;
+  const int64_t total = (s.Np / kTileN) * (s.K / kTileK) * 64;
   int64_t blocks = (total + 255) / 256;
   if (blocks > (1 << 20)) blocks = 1 << 20;
   if (s.has_perm)

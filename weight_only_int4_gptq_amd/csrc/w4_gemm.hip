@@ -442,7 +442,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
     const int i = rr / (NB * 4), s = (rr >> 2) % NB, r = rr & 3;
     const int64_t m = m0 + 16 * i + 4 * (l >> 4) + r;
     const int64_t n = (t0 + s) * kTileN + (l & 15);
-    if (m < M) {
+    if (m < M && n < N) {  // n >= N: the padded half of the last strip
       float o = acc[q];
       if (bias != nullptr) o += act_to_f32<BF16>(bias[n]);
       y[m * N + n] = f32_to_act<BF16>(o);
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, quad = lane >> 4;
-  const int64_t T = N / kTileN;
+  const int64_t T = (N + kTileN - 1) / kTileN;  // strips; the last may be half padding
   const int64_t nblk = K / kTileK;
   // split-K: workgroup z of gridDim.z walks blocks [kb0, kb0 + nb) (nb >= 1:
   // the host never splits finer than one block)
@@ -585,9 +585,9 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
     if ((int64_t)blockIdx.y * C::BM >= M) return;  // uniform: the workgroup leaves before any barrier
     x += r0 * K;
     y += r0 * N;
-    qw += e * (K * N / 32);
-    sc += e * N * G;
-    if (HAS_Z) zs += e * (N / 8) * G;
+    qw += e * (K * T * kTileN / 32);
+    sc += e * T * kTileN * G;
+    if (HAS_Z) zs += e * T * 2 * G;
     if (bias != nullptr) bias += e * N;
     split = 0;
     nsplit = 1;
@@ -751,6 +751,7 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
     const int64_t t = tw0 + nt;
     if (t >= T) continue;
     const int64_t n = t * kTileN + c;
+    if (n >= N) continue;  // the padded half of the last strip
     const float bv = bias != nullptr && pz == nullptr ? act_to_f32<BF16>(bias[n]) : 0.f;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -849,7 +850,9 @@ constexpr int skinny_depth() {
 
 template <int MT, int NB, int KW, int GM, bool BF16, bool HZ, bool HP, bool XL, int D = skinny_depth<MT, NB, XL, HP>()>
 hipError_t run_skinny(const Args& a, hipStream_t st) {
-  const dim3 grid((unsigned)(a.N / (kTileN * NB)), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
+  const int64_t T = (a.N + kTileN - 1) / kTileN;
+  if (T % NB != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(T / NB), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
   if (XL && a.M > kXlRows) return hipErrorInvalidValue;  // staging holds kXlRows rows
   const size_t lds = skinny_lds_bytes(MT, NB, KW, XL, a.M, a.K);
   if (lds > kMaxSkinnyLds) return hipErrorInvalidValue;
@@ -883,7 +886,7 @@ hipError_t launch_gather(const uint16_t* x, const int32_t* perm, uint16_t* xp, i
 template <int MT, int NS, int WN, int S, int GM, bool BF16, bool HZ>
 hipError_t run_wide(const Args& a, const uint16_t* x, hipStream_t st) {
   using C = WideCfg<MT, NS, WN, S>;
-  const int64_t T = a.N / kTileN;
+  const int64_t T = (a.N + kTileN - 1) / kTileN;
   const int splits = a.splits > 1 ? a.splits : 1;
   if (splits > 1 && (a.part == nullptr || splits > a.K / kTileK || a.offs != nullptr)) return hipErrorInvalidValue;
   const int64_t rows = a.offs != nullptr ? a.max_rows : a.M;
@@ -1013,7 +1016,7 @@ GemmPlan plan_gemm(const Shape& s, int64_t M) {
   // needs writes back the XCD's whole L2 on gfx950 and cost far more than it
   // saved at these sizes (measured).
   GemmPlan p;
-  const int64_t T = s.N / kTileN;
+  const int64_t T = s.Np / kTileN;
   if (M <= 4 && skinny_lds_bytes(1, 1, 8, true, M, s.K) <= kMaxSkinnyLds) {
     // activations staged in LDS; few strips (N <= 4096): more waves per strip
     const bool k16 = T <= 256 && skinny_lds_bytes(1, 1, 16, true, M, s.K) <= kMaxSkinnyLds;
@@ -1125,7 +1128,7 @@ GemmPlan plan_moe(const Shape& s, int64_t max_rows, int experts) {
   // grouped launch of the wide kernel (no split-K): 16-row tiles for up to
   // 16 rows per expert, else the largest tile not taller than the rows that
   // still gives >= 256 workgroups over all experts
-  const int64_t T = s.N / kTileN;
+  const int64_t T = s.Np / kTileN;
   int idx = kNumWide - 1;
   if (max_rows <= 16) {
     idx = T * experts >= 1024 ? kWide16x32 : kWide16x16;

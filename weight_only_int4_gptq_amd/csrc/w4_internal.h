@@ -18,6 +18,7 @@ constexpr int kWordsPerBlock = kTileN * kTileK / 8;  // 256
 
 struct Shape {
   int64_t K, N;
+  int64_t Np;  // N padded to whole 16-column strips (the tile layout's column count)
   int gs;  // effective group size (K for per-channel)
   int G;   // number of groups
   bool bf16, has_z, has_perm;
@@ -27,6 +28,7 @@ inline Shape shape_of(const w4_layer* L) {
   Shape s;
   s.K = L->K;
   s.N = L->N;
+  s.Np = (L->N + kTileN - 1) / kTileN * kTileN;
   s.gs = L->group_size == -1 ? (int)L->K : L->group_size;
   s.G = (int)(L->K / s.gs);
   s.bf16 = L->act_dtype == W4_BF16;

@@ -127,8 +127,11 @@ template <bool HAS_Z, bool HAS_PERM>
 __global__ void tile_weights(const uint32_t* __restrict__ sw, const uint32_t* __restrict__ sz,
                              const uint16_t* __restrict__ scales, const int32_t* __restrict__ perm,
                              uint32_t* __restrict__ tw, int64_t K, int64_t N, int gs) {
+  // columns n >= N pad the last strip: codes 8 (their zero point is 8 and
+  // their scale 1, see tile_scales / tile_zeros), so the weight is 0
   const int64_t B = K / kTileK;
-  const int64_t total = K * N / 8;
+  const int64_t Np = (N + kTileN - 1) / kTileN * kTileN;
+  const int64_t total = K * Np / 8;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int j = (int)(idx & 3);
@@ -138,6 +141,10 @@ __global__ void tile_weights(const uint32_t* __restrict__ sw, const uint32_t* __
     const int64_t n = kTileN * t + (l & 15);
     const int64_t k0 = kTileK * b + 32 * j + 8 * (l >> 4);
     const int64_t g = k0 / gs;
+    if (n >= N) {
+      tw[idx] = 0x88888888u;
+      continue;
+    }
     const uint16_t sbits = scales[g * N + n];
     uint32_t word = 0;
     if ((sbits & 0x7FFFu) == 0) {
@@ -164,11 +171,12 @@ __global__ void tile_weights(const uint32_t* __restrict__ sw, const uint32_t* __
 // take the previous group's stored scale.
 __global__ void tile_scales(const uint16_t* __restrict__ s, uint16_t* __restrict__ ts, int64_t N, int G,
                             uint16_t one_bits) {
-  for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < N; n += (int64_t)gridDim.x * blockDim.x) {
+  const int64_t Np = (N + kTileN - 1) / kTileN * kTileN;  // padded columns get scale 1
+  for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < Np; n += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = n / kTileN, c = n - t * kTileN;
     uint16_t prev = one_bits;
     for (int g = 0; g < G; ++g) {
-      const uint16_t v = s[(int64_t)g * N + n];
+      const uint16_t v = n < N ? s[(int64_t)g * N + n] : one_bits;
       const uint16_t out = (v & 0x7FFFu) == 0 ? prev : v;
       ts[(t * G + g) * kTileN + c] = out;
       prev = out;
@@ -176,16 +184,17 @@ __global__ void tile_scales(const uint16_t* __restrict__ s, uint16_t* __restrict
   }
 }
 
-// Tiled zero word (t, g, w) is the standard zero word [g, 2t + w].
+// Tiled zero word (t, g, w) is the standard zero word [g, 2t + w] (eight
+// padded columns, N % 16 == 8: zero points 8).
 __global__ void tile_zeros(const uint32_t* __restrict__ sz, uint32_t* __restrict__ tz, int64_t N, int G) {
-  const int64_t T = N / kTileN;
+  const int64_t T = (N + kTileN - 1) / kTileN;
   const int64_t total = T * G * 2;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int w = (int)(idx & 1);
     const int64_t tg = idx >> 1;
     const int64_t t = tg / G, g = tg - t * G;
-    tz[idx] = sz[g * (N / 8) + 2 * t + w];
+    tz[idx] = 8 * (2 * t + w) < N ? sz[g * (N / 8) + 2 * t + w] : 0x88888888u;
   }
 }
 
@@ -229,7 +238,7 @@ hipError_t launch_status_zero(int32_t* status, hipStream_t st) {
 hipError_t launch_tile(const Shape& s, const int32_t* std_w, const int32_t* std_z, const uint16_t* scales,
                        const int32_t* perm, int32_t* tiled_w, uint16_t* tiled_s, int32_t* tiled_z,
                        hipStream_t st) {
-  const int64_t total = s.K * s.N / 8;
+  const int64_t total = s.K * s.Np / 8;
   const unsigned grid = grid_for(total, 256);
   const uint32_t* sw = reinterpret_cast<const uint32_t*>(std_w);
   const uint32_t* sz = reinterpret_cast<const uint32_t*>(std_z);
@@ -244,11 +253,11 @@ hipError_t launch_tile(const Shape& s, const int32_t* std_w, const int32_t* std_
     tile_weights<false, false><<<grid, 256, 0, st>>>(sw, sz, scales, perm, tw, s.K, s.N, s.gs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  tile_scales<<<grid_for(s.N, 256), 256, 0, st>>>(scales, tiled_s, s.N, s.G, s.bf16 ? 0x3F80 : 0x3C00);
+  tile_scales<<<grid_for(s.Np, 256), 256, 0, st>>>(scales, tiled_s, s.N, s.G, s.bf16 ? 0x3F80 : 0x3C00);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (s.has_z) {
-    tile_zeros<<<grid_for(s.N / kTileN * s.G * 2, 256), 256, 0, st>>>(sz, reinterpret_cast<uint32_t*>(tiled_z),
+    tile_zeros<<<grid_for(s.Np / kTileN * s.G * 2, 256), 256, 0, st>>>(sz, reinterpret_cast<uint32_t*>(tiled_z),
                                                                        s.N, s.G);
     e = hipGetLastError();
   }

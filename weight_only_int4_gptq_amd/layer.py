@@ -64,10 +64,11 @@ class W4A16Linear:
             std_w = torch.empty((K // 8, N), dtype=i32, device=d)
             std_z = torch.empty((G, N // 8), dtype=i32, device=d)
             A.w4_repack_awq(self.layer, qweight, qzeros, std_w, std_z, stream)
+        T = (N + 15) // 16  # strips; a last half strip is padded
         tiled = {
-            "qweight": torch.empty((K * N // 8,), dtype=i32, device=d),
-            "scales": torch.empty((N // 16, G, 16), dtype=_TORCH_DTYPE[self.dtype], device=d),
-            "qzeros": torch.empty((N // 16, G, 2), dtype=i32, device=d) if self.has_zero_points else None,
+            "qweight": torch.empty((K * T * 2,), dtype=i32, device=d),
+            "scales": torch.empty((T, G, 16), dtype=_TORCH_DTYPE[self.dtype], device=d),
+            "qzeros": torch.empty((T, G, 2), dtype=i32, device=d) if self.has_zero_points else None,
             "perm": torch.empty((K,), dtype=i32, device=d) if self.has_g_idx else None,
         }
         status = torch.empty((1,), dtype=i32, device=d) if self.has_g_idx else None
