@@ -38,6 +38,8 @@
 // results are summed in LDS at the end.  Each scale period (one group, at
 // most 128 rows) is accumulated exactly in fp32 from integer operands and
 // then added, times its fp32 scale, to the fp32 total.
+#include <atomic>
+
 #include "w4_internal.h"
 
 namespace w4 {
@@ -857,11 +859,19 @@ hipError_t run_skinny(const Args& a, hipStream_t st) {
   const size_t lds = skinny_lds_bytes(MT, NB, KW, XL, a.M, a.K);
   if (lds > kMaxSkinnyLds) return hipErrorInvalidValue;
   if (lds > 64 * 1024) {
-    // dynamic LDS beyond 64 KiB has to be allowed per kernel (once)
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_skinny<MT, NB, KW, GM, BF16, HZ, HP, XL, D>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxSkinnyLds);
-    if (attr != hipSuccess) return attr;
+    // dynamic LDS beyond 64 KiB has to be allowed per kernel and device
+    // (once each; devices past 64 are allowed on every call)
+    static std::atomic<uint64_t> allowed{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+    if (bit == 0 || (allowed.load(std::memory_order_relaxed) & bit) == 0) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_skinny<MT, NB, KW, GM, BF16, HZ, HP, XL, D>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxSkinnyLds);
+      if (e != hipSuccess) return e;
+      allowed.fetch_or(bit, std::memory_order_relaxed);
+    }
   }
   gemm_skinny<MT, NB, KW, GM, BF16, HZ, HP, XL, D><<<grid, 64 * KW, lds, st>>>(
       a.x, a.qw, a.sc, a.zs, a.perm, a.bias, a.y, a.M, a.K, a.N, a.G);
