@@ -62,11 +62,12 @@ typedef struct {
   size_t qzeros;        /* int32 [G][N/8]   AWQ or standard zero words (0 if none) */
   size_t scales;        /* act   [G][N]     scales as loaded                       */
   size_t std_qweight;   /* int32 [K/8][N]   standard qweight (packed along K)      */
-  size_t tiled_qweight; /* int32 K*Np/8     tile layout (see w4_repack_gptq)       */
-  size_t tiled_scales;  /* act   [Np/16][G][16]                                     */
-  size_t tiled_qzeros;  /* int32 [Np/16][G][2] (0 if no zero points)               */
+  size_t tiled_qweight; /* int32 Kp*Np/8    tile layout (see w4_repack_gptq)       */
+  size_t tiled_scales;  /* act   [Np/16][Gp][16]                                    */
+  size_t tiled_qzeros;  /* int32 [Np/16][Gp][2] (0 if no zero points)              */
   /* Np = N rounded up to a multiple of 16 (the tile layout pads a last half
-   * strip when N % 16 == 8) */
+   * strip when N % 16 == 8); Kp = K rounded up to a multiple of 128 (padded
+   * rows when K % 128 != 0); Gp = Kp / group_size (1 for group_size -1) */
   size_t perm;          /* int32 [K] act-order row permutation (0 without g_idx)   */
 } w4_sizes_t;
 
@@ -75,8 +76,12 @@ typedef struct {
  *   W4_ERR_INVALID_ARGUMENT  layer == NULL, K <= 0, N <= 0;
  *   W4_ERR_UNSUPPORTED       group_size not in {-1, 32, 64, 128} (the group
  *                            sizes listed in section 5.3 of the vLLM AWQ
- *                            practice page), K % 128 != 0, N % 8 != 0,
- *                            K % group_size != 0, act_dtype not fp16/bf16,
+ *                            practice page), K % 32 != 0, N % 8 != 0,
+ *                            K % group_size != 0, K % 128 != 0 with
+ *                            group_size 128 or act-order (a K tail is
+ *                            padded to whole 128-row blocks, which needs
+ *                            whole groups and the natural row order),
+ *                            act_dtype not fp16/bf16,
  *                            has_g_idx with group_size == -1, K > 2^20 or
  *                            N > 2^20.
  * Host only; never touches the GPU. */
@@ -86,8 +91,8 @@ w4_status w4_check_layer(const w4_layer* layer);
 w4_status w4_sizes(const w4_layer* layer, w4_sizes_t* out);
 
 /* Bytes of scratch device memory w4a16_linear needs for M rows (0 when the
- * chosen kernel needs none: M <= 16 without act-order, M > 256, or layers
- * with N > 16384 and no act-order).  Host only. */
+ * chosen kernel needs none: K % 128 == 0 and M <= 16 without act-order,
+ * M > 256, or layers with N > 16384 and no act-order).  Host only. */
 w4_status w4_workspace_size(const w4_layer* layer, int64_t M, size_t* bytes);
 
 /* Name of the kernel w4a16_linear launches for M rows (the analogue of the
@@ -121,9 +126,9 @@ w4_status w4_repack_awq(const w4_layer* layer, const int32_t* awq_qweight, const
  *   std_qzeros     int32 [G][N/8]      (device; NULL iff !has_zero_points)
  *   scales         act   [G][N]        (device)
  *   g_idx          int32 [K]           (device; NULL iff !has_g_idx)
- *   tiled_qweight  int32 [K*N/8]       (device, 16-byte aligned) -- written
- *   tiled_scales   act   [Np/16][G][16] (device) -- written
- *   tiled_qzeros   int32 [Np/16][G][2]  (device; NULL iff !has_zero_points) -- written
+ *   tiled_qweight  int32 [Kp*Np/8]     (device, 16-byte aligned) -- written
+ *   tiled_scales   act   [Np/16][Gp][16] (device) -- written
+ *   tiled_qzeros   int32 [Np/16][Gp][2] (device; NULL iff !has_zero_points) -- written
  *   perm           int32 [K]           (device; NULL iff !has_g_idx) -- written
  *   status_dev     int32 [1]           (device; may be NULL) -- written:
  *                  bit 0 = a g_idx entry outside [0, G); bit 1 = some group
@@ -134,11 +139,14 @@ w4_status w4_repack_awq(const w4_layer* layer, const int32_t* awq_qweight, const
  * (perm[k'] = original row of sorted row k'); a scale equal to zero is
  * replaced by the previous group's stored scale (1.0 for group 0) and the
  * codes of that group and column by its zero point; word [t][b][l][j]
- * (t < Np/16, b < K/128, l < 64, j < 4) holds column 16t + l%16 at sorted
+ * (t < Np/16, b < Kp/128, l < 64, j < 4) holds column 16t + l%16 at sorted
  * rows 128b + 32j + 8(l/16) + e, e = 0..7, K-offset e in nibble slot
  * [0,4,1,5,2,6,3,7][e].  Columns N .. Np-1 (a padded half strip) hold codes
  * and zero points 8 and scale 1: their weights are 0 and no output column
- * is written for them. */
+ * is written for them.  Rows K .. Kp-1 (a padded last block) hold codes
+ * equal to their zero point: the layer's zero point with group_size -1,
+ * else 8 in the padded groups G .. Gp-1, whose scales are 1 and zero
+ * points 8; their weights are 0. */
 w4_status w4_repack_gptq(const w4_layer* layer, const int32_t* std_qweight, const int32_t* std_qzeros,
                          const void* scales, const int32_t* g_idx, int32_t* tiled_qweight,
                          void* tiled_scales, int32_t* tiled_qzeros, int32_t* perm, int32_t* status_dev,
@@ -158,7 +166,8 @@ w4_status w4_repack_gptq(const w4_layer* layer, const int32_t* std_qweight, cons
  *   workspace      device scratch of >= w4_workspace_size() bytes (16-byte
  *                  aligned), or NULL when that size is 0; no initialization
  *                  needed.  With act-order it receives x with its columns
- *                  gathered through perm; for 16 < M <= 256 on layers with
+ *                  gathered through perm; with K % 128 != 0, x padded with
+ *                  zero columns to Kp; for 16 < M <= 256 on layers with
  *                  N <= 16384 it also holds the fp32 split-K partials
  *                  [splits][M][N].  Calls that overlap in time must not
  *                  share a workspace.
@@ -171,8 +180,8 @@ w4_status w4a16_linear(const w4_layer* layer, int64_t M, const void* x, const in
 /* Grouped W4A16 linear for mixture-of-experts layers (the WNA16 MoE path of
  * the vLLM AWQ practice page, section 5.4, and of the SGLang quantization
  * page's MoE section): num_experts experts share one w4_layer description
- * (K, N, group size, zero points, dtype; act-order is not supported and
- * returns W4_ERR_UNSUPPORTED), each with its own tiled weights, and
+ * (K, N, group size, zero points, dtype; act-order and K % 128 != 0 are
+ * not supported and return W4_ERR_UNSUPPORTED), each with its own tiled weights, and
  *   y[r] = x[r] W_e (+ bias_e)   for every row r of expert e.
  *   x              act [total_rows][K] row-major (device, 16-byte aligned):
  *                  the rows routed to each expert, grouped by expert (the

@@ -339,12 +339,17 @@ def _one_bits(dtype: str) -> int:
 def tile_layout(std_qweight, std_qzeros, scales, group_size: int, dtype: str, g_idx=None) -> dict:
     """Repack standard weights into the tile layout consumed by the kernels.
 
-    Definition (K % 128 == 0, N % 8 == 0, g = K when group_size == -1,
+    Definition (K % 32 == 0, N % 8 == 0, g = K when group_size == -1,
     G = K / g, every act-order group owning exactly g rows).  The column
     count is padded to Np = 16 ceil(N / 16) (the pages' tile padding, read
     as: a padded column has every code and its zero point equal to 8 and
-    every scale equal to 1, so its weights are exactly 0); steps 3-5 then
-    run over Np columns:
+    every scale equal to 1, so its weights are exactly 0).  The row count
+    is padded the same way to Kp = 128 ceil(K / 128) (no act-order then):
+    a padded row's code equals its zero point, which is the column's zero
+    point when the layer has one group (per-channel, g = K) and 8 in the
+    Gp - G padded groups (Gp = Kp / g) otherwise, whose scales are 1 and
+    zero points 8.  Steps 3-5 then run over Kp rows, Gp groups and Np
+    columns:
 
     1. Row order: perm = stable argsort of g_idx (identity without g_idx);
        sorted row k' holds original row perm[k'] and lies in group k' // g.
@@ -365,7 +370,8 @@ def tile_layout(std_qweight, std_qzeros, scales, group_size: int, dtype: str, g_
     """
     q = unpack_std(std_qweight)
     K, N = q.shape
-    assert K % TILE_K == 0 and N % 8 == 0
+    assert K % 32 == 0 and N % 8 == 0
+    assert K % TILE_K == 0 or g_idx is None
     gs = K if group_size == -1 else group_size
     G = K // gs
     z = None if std_qzeros is None else unpack_std_zeros(std_qzeros)
@@ -399,6 +405,23 @@ def tile_layout(std_qweight, std_qzeros, scales, group_size: int, dtype: str, g_
         if z is not None:
             z = np.concatenate([z, np.full((G, Np - N), 8, dtype=np.int64)], axis=1)
     N = Np
+
+    # Padding to Kp rows: per-channel rows take the column's zero point,
+    # grouped rows fill new groups with zero points 8 and scales 1.
+    Kp = -(-K // TILE_K) * TILE_K
+    if Kp != K:
+        if G == 1 and gs == K:
+            zrow = np.full(N, 8, dtype=np.int64) if z is None else z[0]
+            pad_codes = np.broadcast_to(zrow, (Kp - K, N))
+        else:
+            pad_codes = np.full((Kp - K, N), 8, dtype=np.int64)
+            Gp = Kp // gs
+            stored = np.concatenate([stored, np.full((Gp - G, N), _one_bits(dtype), dtype=np.int64)], axis=0)
+            if z is not None:
+                z = np.concatenate([z, np.full((Gp - G, N), 8, dtype=np.int64)], axis=0)
+            G = Gp
+        q = np.concatenate([q, np.asarray(pad_codes, dtype=np.int64)], axis=0)
+    K = Kp
 
     # Step 3: words [t, b, l, j] built from explicit index arithmetic.
     T, B = N // TILE_N, K // TILE_K

@@ -82,6 +82,13 @@ REPACK_VARIANTS = [
     # N % 16 == 8: the last strip is half padding
     ("fp16-g128-z-n264", 384, 264, 128, True, False, "fp16", False),
     ("bf16-g64-sym-act-n40", 512, 40, 64, False, True, "bf16", True),
+    # K % 128 != 0: the last 128-row block is padded (new groups, or the
+    # per-channel group)
+    ("fp16-g32-z-k96", 96, 48, 32, True, False, "fp16", False),
+    ("bf16-g64-sym-k320-zeroscales", 320, 40, 64, False, False, "bf16", True),
+    ("fp16-ch-z-k224", 224, 48, -1, True, False, "fp16", False),
+    ("bf16-ch-z-k1056-zeroscales", 1056, 264, -1, True, False, "bf16", True),
+    ("fp16-g32-z-k1120-zeroscales", 1120, 64, 32, True, False, "fp16", True),
 ]
 
 
@@ -109,16 +116,17 @@ def test_repack_gptq_bit_exact(W, v):
     import torch
     name, K, N, gs, has_z, has_g, dtype, zs = v
     say(f"repack_gptq {name}")
-    G = 1 if gs == -1 else K // gs
     sw, sz, s, gi = _std_layer_inputs(K, N, gs, has_z, has_g, dtype, zs)
     ref = O.tile_layout(sw, sz, s, gs, dtype, g_idx=gi)
     L = W.make_layer(K, N, gs, has_z, has_g, dtype)
     outs = []
     T = (N + 15) // 16
+    Kp = -(-K // 128) * 128
+    Gp = 1 if gs == -1 else Kp // gs
     for fill in (0x00, 0xFF):
-        tw = filled((K * T * 2,), torch.int32, fill)
-        ts = filled((T, G, 16), act_dtype(dtype), fill)
-        tz = filled((T, G, 2), torch.int32, fill) if has_z else None
+        tw = filled((Kp * T * 2,), torch.int32, fill)
+        ts = filled((T, Gp, 16), act_dtype(dtype), fill)
+        tz = filled((T, Gp, 2), torch.int32, fill) if has_z else None
         pm = filled((K,), torch.int32, fill) if has_g else None
         st = filled((1,), torch.int32, fill)
         W.w4_repack_gptq(L, to_dev(sw), to_dev(sz) if has_z else None, to_dev(s), to_dev(gi) if has_g else None,
@@ -241,6 +249,12 @@ LINEAR_VARIANTS = [
     ("awq-fp16-g128-n264-bias", "awq", 384, 264, 128, True, False, "fp16", True),
     ("std-bf16-g32-z-n40", "std", 512, 40, 32, True, False, "bf16", False),
     ("std-fp16-g128-z-act-n24", "std", 512, 24, 128, True, True, "fp16", True),
+    # K % 128 != 0 (zero-padded activations, padded weight rows)
+    ("std-fp16-g32-z-k1120-bias", "std", 1120, 272, 32, True, False, "fp16", True),
+    ("awq-bf16-g64-z-k320-n264", "awq", 320, 264, 64, True, False, "bf16", False),
+    ("std-fp16-ch-z-k224", "std", 224, 272, -1, True, False, "fp16", False),
+    ("std-bf16-ch-sym-k96-n40", "std", 96, 40, -1, False, False, "bf16", True),
+    ("std-fp16-g32-sym-k32", "std", 32, 48, 32, False, False, "fp16", False),
 ]
 LINEAR_MS = (1, 3, 16, 17, 33, 64, 70, 130)
 
@@ -388,20 +402,22 @@ def test_linear_full_size_sampled(W, c, M):
 WIDE_TILE_SHAPES = [(1024, 16384), (256, 32768), (64, 32768), (32, 32768), (40, 8192), (24, 8192), (200, 8192),
                     (16, 12288), (9, 20480), (300, 4104), (16, 16392)]
 WIDE_VARIANTS = [
-    # (name, fmt, group_size, has_zeros, has_gidx, dtype)
-    ("awq-fp16-g128", "awq", 128, True, False, "fp16"),
-    ("std-bf16-g128-sym", "std", 128, False, False, "bf16"),
-    ("std-fp16-g32-z", "std", 32, True, False, "fp16"),
-    ("std-bf16-g64-z", "std", 64, True, False, "bf16"),
-    ("std-fp16-ch-z", "std", -1, True, False, "fp16"),
-    ("std-fp16-g128-z-act", "std", 128, True, True, "fp16"),
+    # (name, fmt, group_size, has_zeros, has_gidx, dtype, K)
+    ("awq-fp16-g128", "awq", 128, True, False, "fp16", 1152),
+    ("std-bf16-g128-sym", "std", 128, False, False, "bf16", 1152),
+    ("std-fp16-g32-z", "std", 32, True, False, "fp16", 1152),
+    ("std-bf16-g64-z", "std", 64, True, False, "bf16", 1152),
+    ("std-fp16-ch-z", "std", -1, True, False, "fp16", 1152),
+    ("std-fp16-g128-z-act", "std", 128, True, True, "fp16", 1152),
+    # K tails: nine blocks after padding, the last one partly padding
+    ("awq-fp16-g32-z-k1120", "awq", 32, True, False, "fp16", 1120),
+    ("std-bf16-ch-sym-k1056", "std", -1, False, False, "bf16", 1056),
 ]
 
 
 @pytest.mark.parametrize("v", WIDE_VARIANTS, ids=[v[0] for v in WIDE_VARIANTS])
 def test_linear_wide_tiles_sampled(W, v):
-    name, fmt, gs, has_z, has_g, dtype = v
-    K = 1152
+    name, fmt, gs, has_z, has_g, dtype, K = v
     G = 1 if gs == -1 else K // gs
     lo, hi = (0.002, 0.02) if dtype == "fp16" else (0.001, 0.01)
     for M, N in WIDE_TILE_SHAPES:

@@ -64,6 +64,17 @@ def test_check_layer_status_codes(W):
     s = W.w4_sizes(W.make_layer(512, 24, 128, True, False, "fp16"))
     assert s["tiled_qweight"] == 512 * 32 // 2 and s["tiled_scales"] == 4 * 32 * 2
     assert s["tiled_qzeros"] == 2 * 4 * 2 * 4 and s["std_qweight"] == 64 * 24 * 4
+    # K % 128 != 0 (K % 32 == 0) is accepted for group sizes 32, 64 and
+    # per-channel without act-order: the tile layout pads rows to Kp
+    for K, gs in ((96, 32), (320, 64), (320, -1), (32, -1), (1120, 32)):
+        assert W.w4_check_layer(W.make_layer(K, 256, gs, True, False, "fp16")) == W.W4_OK, (K, gs)
+    for K, gs, gi in ((320, 64, True), (672, 128, False), (336, 32, False), (96, 32, True)):
+        assert W.w4_check_layer(W.make_layer(K, 256, gs, True, gi, "fp16")) == W.W4_ERR_UNSUPPORTED, (K, gs, gi)
+    s = W.w4_sizes(W.make_layer(320, 24, 64, True, False, "fp16"))
+    assert s["tiled_qweight"] == 384 * 32 // 2 and s["tiled_scales"] == 6 * 32 * 2
+    assert s["tiled_qzeros"] == 2 * 6 * 2 * 4 and s["std_qweight"] == 40 * 24 * 4 and s["scales"] == 5 * 24 * 2
+    s = W.w4_sizes(W.make_layer(320, 256, -1, True, False, "bf16"))
+    assert s["tiled_qweight"] == 384 * 256 // 2 and s["tiled_scales"] == 256 * 2 and s["tiled_qzeros"] == 16 * 2 * 4
 
 
 def test_sizes_of_the_tiny_layer(W):
@@ -88,6 +99,10 @@ def test_workspace_and_kernel_name(W):
     assert W.w4_kernel_name(L, -3) == "invalid"
     assert W.w4_kernel_name(W.make_layer(100, 16), 1) == "invalid"
     assert W.w4_kernel_name(L, 1).startswith("w4_")
+    # a K tail needs the zero-padded activations in the workspace
+    Lt = W.make_layer(320, 256, 64, True, False, "fp16")
+    assert W.w4_workspace_size(Lt, 4) >= 4 * 384 * 2 and W.w4_kernel_name(Lt, 4).startswith("w4_")
+    assert W.w4_workspace_size(W.make_layer(384, 256, 64, True, False, "fp16"), 4) == 0
     for s in range(5):
         assert W.w4_status_str(s)
     assert W.w4_status_str(99) == "unknown status"
@@ -154,3 +169,10 @@ def test_split_k_workspace_is_sized_and_checked(W):
     need = W.w4_workspace_size(L, 32)
     assert _lin(W, L, 32, qz=None, ws=16, ws_bytes=need - 1) == W.W4_ERR_WORKSPACE
     assert _lin(W, L, 32, qz=None, ws=None, ws_bytes=0) == W.W4_ERR_WORKSPACE
+
+
+def test_moe_rejects_k_tails_and_act_order(W):
+    # the grouped launch runs whole 128-row blocks only, without act-order
+    for L in (W.make_layer(320, 256, 64, True, False, "fp16"), W.make_layer(512, 256, 128, True, True, "fp16")):
+        st = W.lib().w4a16_moe_linear(ctypes.byref(L), 2, 8, 4, 16, 16, 16, 16, 16, None, 16, None)
+        assert st == W.W4_ERR_UNSUPPORTED

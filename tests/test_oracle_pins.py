@@ -446,6 +446,46 @@ def test_tile_layout_pads_columns_to_whole_strips():
     assert (Wp[:, N:] == 0).all()
 
 
+@pytest.mark.parametrize("K,gs,has_z", [(96, 32, True), (192, 64, False), (320, 64, True), (224, -1, True), (32, -1, False)])
+def test_tile_layout_pads_rows_to_whole_blocks(K, gs, has_z):
+    # K % 128 != 0: rows K .. Kp-1 are padded.  A padded row's code equals
+    # its zero point, so every padded weight is exactly 0; grouped layers
+    # get new groups (scale 1, zero point 8), a per-channel layer keeps its
+    # one group and its zero point
+    N = 16
+    Kp = -(-K // 128) * 128
+    g = K if gs == -1 else gs
+    G, Gp = K // g, (1 if gs == -1 else Kp // g)
+    rng = seeded(921)
+    sw = random_words(rng, (K // 8, N))
+    sz = random_words(rng, (G, N // 8)) if has_z else None
+    sc = uniform_scales(rng, (G, N), 0.002, 0.02, "fp16")
+    t = O.tile_layout(sw, sz, sc, gs, "fp16")
+    assert t["qweight"].size == Kp * N // 8 and t["scales"].shape == (1, Gp, 16)
+    full = O.untile_codes(t["qweight"], Kp, N)
+    np.testing.assert_array_equal(full[:K], O.unpack_std(sw))
+    q, z = O.codes_from_inputs("std", sw, sz)
+    if gs == -1:
+        want = np.broadcast_to(z[0] if has_z else np.full(N, 8), (Kp - K, N))
+        np.testing.assert_array_equal(full[K:], want)
+    else:
+        assert (full[K:] == 8).all()
+        assert (t["scales"][0, G:] == 0x3C00).all()
+        if has_z:
+            assert (O.u32(t["zeros"])[0, G:] == 0x88888888).all()
+    np.testing.assert_array_equal(t["scales"][0, :G], sc.view(np.uint16))
+    # dequantizing the padded layout gives the layer's weights and zero rows
+    sp = O.half_to_f64(t["scales"][0].view(np.float16))
+    zp = None
+    if has_z:
+        zw = O.u32(t["zeros"])[0]
+        zp = np.array([[(int(zw[gg, c // 8]) >> (4 * (c % 8))) & 0xF for c in range(N)] for gg in range(Gp)])
+    Wp = O.dequant(full, zp, sp, O.group_index(Kp, Kp if gs == -1 else gs))
+    W = O.dequant(q, z, O.half_to_f64(sc), O.group_index(K, gs))
+    np.testing.assert_array_equal(Wp[:K], W)
+    assert (Wp[K:] == 0).all()
+
+
 # ----------------------------------------------------------------------------
 # Grouped (mixture-of-experts) reference
 # ----------------------------------------------------------------------------

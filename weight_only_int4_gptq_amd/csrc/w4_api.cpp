@@ -44,7 +44,10 @@ w4_status w4_check_layer(const w4_layer* L) {
   const int gs = L->group_size;
   if (gs != -1 && gs != 32 && gs != 64 && gs != 128) return W4_ERR_UNSUPPORTED;
   if (L->K > kMaxDim || L->N > kMaxDim) return W4_ERR_UNSUPPORTED;
-  if (L->K % w4::kTileK != 0 || L->N % 8 != 0) return W4_ERR_UNSUPPORTED;  // N tail: padded strip
+  // N tail: a padded last strip.  K tail (K % 128 != 0): padded rows, for
+  // K % 32 == 0 with group sizes 32, 64 or per-channel and no act-order
+  if (L->N % 8 != 0 || L->K % 32 != 0) return W4_ERR_UNSUPPORTED;
+  if (L->K % w4::kTileK != 0 && (gs == 128 || L->has_g_idx)) return W4_ERR_UNSUPPORTED;
   if (gs != -1 && L->K % gs != 0) return W4_ERR_UNSUPPORTED;
   if (L->has_g_idx && gs == -1) return W4_ERR_UNSUPPORTED;
   return W4_OK;
@@ -60,10 +63,10 @@ w4_status w4_sizes(const w4_layer* L, w4_sizes_t* out) {
   out->qzeros = s.has_z ? G * (N / 8) * 4 : 0;
   out->scales = G * N * 2;
   out->std_qweight = (K / 8) * N * 4;
-  const size_t Np = (size_t)s.Np;
-  out->tiled_qweight = K * Np / 2;
-  out->tiled_scales = G * Np * 2;
-  out->tiled_qzeros = s.has_z ? (Np / w4::kTileN) * G * 2 * 4 : 0;
+  const size_t Np = (size_t)s.Np, Kp = (size_t)s.Kp, Gp = (size_t)s.Gp;
+  out->tiled_qweight = Kp * Np / 2;
+  out->tiled_scales = Gp * Np * 2;
+  out->tiled_qzeros = s.has_z ? (Np / w4::kTileN) * Gp * 2 * 4 : 0;
   out->perm = s.has_perm ? K * 4 : 0;
   return W4_OK;
 }
@@ -80,7 +83,7 @@ w4_status w4_workspace_size(const w4_layer* L, int64_t M, size_t* bytes) {
 const char* w4_kernel_name(const w4_layer* L, int64_t M) {
   if (w4_check_layer(L) != W4_OK || M < 0 || M > kMaxM) return "invalid";
   if (M == 0) return "none";
-  return w4::plan_gemm(w4::shape_of(L), M).name;
+  return w4::plan_gemm(w4::padded_k(w4::shape_of(L)), M).name;
 }
 
 const char* w4_status_str(w4_status s) {
@@ -170,7 +173,7 @@ w4_status w4a16_moe_linear(const w4_layer* L, int32_t num_experts, int64_t total
   w4_status st = w4_check_layer(L);
   if (st != W4_OK) return st;
   const Shape s = w4::shape_of(L);
-  if (s.has_perm) return W4_ERR_UNSUPPORTED;  // act-order experts are not supported
+  if (s.has_perm || s.K != s.Kp) return W4_ERR_UNSUPPORTED;  // act-order experts, K tails
   if (num_experts < 0 || total_rows < 0 || max_rows < 0) return W4_ERR_INVALID_ARGUMENT;
   if (num_experts > 65535 || total_rows > kMaxM) return W4_ERR_UNSUPPORTED;
   if (num_experts == 0 || total_rows == 0) return W4_OK;

@@ -41,9 +41,10 @@ __global__ __launch_bounds__(256) void dequant_dense_kernel(const uint4* __restr
                                                               const uint16_t* __restrict__ ts,
                                                               const uint32_t* __restrict__ tz,
                                                               const int32_t* __restrict__ perm,
-                                                              uint16_t* __restrict__ w, int64_t K, int64_t N,
-                                                              int G, int gs) {
-  const int64_t nblk = K / kTileK;
+                                                              uint16_t* __restrict__ w, int64_t K, int64_t Kp,
+                                                              int64_t N, int G, int gs) {
+  // K, N: the layer; Kp, G, gs: the tile layout's padded rows and groups
+  const int64_t nblk = Kp / kTileK;
   const int64_t total = ((N + kTileN - 1) / kTileN) * nblk * 64;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256) void dequant_dense_kernel(const uint4* __restr
         const uint32_t slot = (0x73625140u >> (4 * e)) & 0xFu;
         const int q = (int)((words[j] >> (4 * slot)) & 0xFu);
         const int64_t k = HAS_PERM ? (int64_t)perm[k0 + e] : k0 + e;
-        if (HAS_PERM && (uint64_t)k >= (uint64_t)K) continue;  // a perm entry out of range writes nothing
+        if ((uint64_t)k >= (uint64_t)K) continue;  // a padded row, or a perm entry out of range: nothing written
         w[k * N + n] = f32_act<BF16>((float)(q - z) * s);
       }
     }
@@ -76,14 +77,16 @@ __global__ __launch_bounds__(256) void dequant_dense_kernel(const uint4* __restr
 template <bool BF16, bool HZ>
 hipError_t launch_dq(const Shape& s, const uint4* tw, const uint16_t* ts, const uint32_t* tz, const int32_t* perm,
                      uint16_t* w, hipStream_t st) {
-  const int64_t total = (s.Np / kTileN) * (s.K / kTileK) * 64;
+  const Shape p = padded_k(s);
+  const int64_t total = (s.Np / kTileN) * (p.K / kTileK) * 64;
   int64_t blocks = (total + 255) / 256;
   if (blocks > (1 << 20)) blocks = 1 << 20;
   if (s.has_perm)
-    dequant_dense_kernel<BF16, HZ, true><<<(unsigned)blocks, 256, 0, st>>>(tw, ts, tz, perm, w, s.K, s.N, s.G, s.gs);
+    dequant_dense_kernel<BF16, HZ, true><<<(unsigned)blocks, 256, 0, st>>>(tw, ts, tz, perm, w, s.K, p.K, s.N, p.G,
+                                                                           p.gs);
   else
-    dequant_dense_kernel<BF16, HZ, false><<<(unsigned)blocks, 256, 0, st>>>(tw, ts, tz, perm, w, s.K, s.N, s.G,
-                                                                            s.gs);
+    dequant_dense_kernel<BF16, HZ, false><<<(unsigned)blocks, 256, 0, st>>>(tw, ts, tz, perm, w, s.K, p.K, s.N, p.G,
+                                                                            p.gs);
   return hipGetLastError();
 }
 

@@ -802,6 +802,19 @@ __global__ void split_reduce(const float* __restrict__ part, const uint16_t* __r
   }
 }
 
+// xp[m][k] = k < K ? x[m][k] : 0 for k < Kp: the activations of a layer
+// whose K is not a whole number of 128-row blocks, padded with zeros (the
+// padded weight rows are zero too), eight halves per thread.
+__global__ void pad_columns(const uint4* __restrict__ x, uint4* __restrict__ xp, int64_t M, int64_t K8,
+                            int64_t Kp8) {
+  const int64_t total = M * Kp8;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = idx / Kp8, k8 = idx - m * Kp8;
+    xp[idx] = k8 < K8 ? x[m * K8 + k8] : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
 // x_perm[m][k'] = x[m][perm[k']] for the act-order wide path (perm entries
 // outside [0, K) read column 0).
 __global__ void gather_columns(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
@@ -969,14 +982,20 @@ hipError_t wide_dispatch(int idx, const Shape& s, const Args& a, const uint16_t*
   }
 }
 
-// Workspace of a call: the gathered activations (act-order, every path but
-// the LDS-staged skinny kernel) first, then the split-K partials.
-inline size_t gather_bytes(const Shape& s, const GemmPlan& p, int64_t M) {
-  return s.has_perm && !p.xl ? ((size_t)M * (size_t)s.K * sizeof(uint16_t) + 255) / 256 * 256 : 0;
+// Workspace of a call: first the activations the kernels read instead of x
+// (gathered through perm with act-order on every path but the LDS-staged
+// skinny kernel; or padded to whole 128-row blocks when K % 128 != 0; the
+// two never coincide), then the split-K partials.
+inline size_t front_bytes(const Shape& s, const GemmPlan& p, int64_t M) {
+  size_t b = 0;
+  if (s.has_perm && !p.xl) b = (size_t)M * (size_t)s.K * sizeof(uint16_t);
+  else if (s.K != s.Kp) b = (size_t)M * (size_t)s.Kp * sizeof(uint16_t);
+  return (b + 255) / 256 * 256;
 }
 
-// Act-order first gathers the columns of x into the workspace.
-hipError_t launch_wide(const Shape& s, const GemmPlan& p, const Args& a0, void* ws, hipStream_t st) {
+// Act-order first gathers the columns of x into the workspace (front bytes
+// of the workspace in use by the caller: `front`).
+hipError_t launch_wide(const Shape& s, const GemmPlan& p, const Args& a0, void* ws, size_t front, hipStream_t st) {
   Args a = a0;
   const uint16_t* x = a.x;
   if (s.has_perm) {
@@ -986,7 +1005,7 @@ hipError_t launch_wide(const Shape& s, const GemmPlan& p, const Args& a0, void* 
     x = xp;
   }
   a.splits = p.splits;
-  a.part = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + gather_bytes(s, p, a.M)) : nullptr;
+  a.part = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + front) : nullptr;
   return wide_dispatch(p.wide, s, a, x, st);
 }
 
@@ -1090,15 +1109,16 @@ GemmPlan plan_gemm(const Shape& s, int64_t M) {
 }
 
 size_t gemm_workspace_bytes(const Shape& s, int64_t M) {
-  const GemmPlan p = plan_gemm(s, M);
+  const GemmPlan p = plan_gemm(padded_k(s), M);
   const size_t part = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)s.N * sizeof(float) : 0;
-  const size_t total = gather_bytes(s, p, M) + part;
-  return total;
+  return front_bytes(s, p, M) + part;
 }
 
-hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* tiled_w, const void* tiled_s,
+hipError_t launch_gemm(const Shape& s0, int64_t M, const void* x, const int32_t* tiled_w, const void* tiled_s,
                        const int32_t* tiled_z, const int32_t* perm, const void* bias, void* y, void* ws,
                        hipStream_t st) {
+  // the kernels run the padded shape (K a whole number of blocks)
+  const Shape s = padded_k(s0);
   Args a;
   a.x = static_cast<const uint16_t*>(x);
   a.qw = reinterpret_cast<const u4*>(tiled_w);
@@ -1118,7 +1138,20 @@ hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* 
   a.G = s.G;
   a.gs = s.gs;
   const GemmPlan p = plan_gemm(s, M);
-  if (p.kind == GemmKind::kWide) return launch_wide(s, p, a, ws, st);
+  const size_t front = front_bytes(s0, p, M);
+  if (s0.K != s0.Kp) {
+    // zero-padded copy of x in the workspace (act-order is excluded here)
+    uint16_t* xp = static_cast<uint16_t*>(ws);
+    const int64_t total = M * (s.K / 8);
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    pad_columns<<<(unsigned)blocks, 256, 0, st>>>(reinterpret_cast<const uint4*>(a.x), reinterpret_cast<uint4*>(xp),
+                                                  M, s0.K / 8, s.K / 8);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.x = xp;
+  }
+  if (p.kind == GemmKind::kWide) return launch_wide(s, p, a, ws, front, st);
   Shape sk = s;
   if (s.has_perm && !p.xl) {
     // gather x[:, perm] into the workspace, then run without act-order

@@ -19,6 +19,8 @@ constexpr int kWordsPerBlock = kTileN * kTileK / 8;  // 256
 struct Shape {
   int64_t K, N;
   int64_t Np;  // N padded to whole 16-column strips (the tile layout's column count)
+  int64_t Kp;  // K padded to whole 128-row blocks (the tile layout's row count)
+  int Gp;      // groups of the padded rows (G, plus the groups of rows K .. Kp-1)
   int gs;  // effective group size (K for per-channel)
   int G;   // number of groups
   bool bf16, has_z, has_perm;
@@ -29,12 +31,24 @@ inline Shape shape_of(const w4_layer* L) {
   s.K = L->K;
   s.N = L->N;
   s.Np = (L->N + kTileN - 1) / kTileN * kTileN;
+  s.Kp = (L->K + kTileK - 1) / kTileK * kTileK;
   s.gs = L->group_size == -1 ? (int)L->K : L->group_size;
   s.G = (int)(L->K / s.gs);
+  s.Gp = L->group_size == -1 ? 1 : (int)(s.Kp / s.gs);
   s.bf16 = L->act_dtype == W4_BF16;
   s.has_z = L->has_zero_points != 0;
   s.has_perm = L->has_g_idx != 0;
   return s;
+}
+
+// The shape the GEMM kernels run: K and the groups padded to whole blocks
+// (padded rows carry zero weights; activations are padded with zeros).
+inline Shape padded_k(const Shape& s) {
+  Shape p = s;
+  p.K = s.Kp;
+  p.G = s.Gp;
+  if (s.Gp == 1) p.gs = (int)s.Kp;  // per-channel: one group of all rows
+  return p;
 }
 
 // ---- repack launchers (w4_repack.hip) ----

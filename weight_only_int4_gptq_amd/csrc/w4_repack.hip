@@ -126,12 +126,14 @@ __global__ __launch_bounds__(kPermThreads) void actorder_perm_kernel(const int32
 template <bool HAS_Z, bool HAS_PERM>
 __global__ void tile_weights(const uint32_t* __restrict__ sw, const uint32_t* __restrict__ sz,
                              const uint16_t* __restrict__ scales, const int32_t* __restrict__ perm,
-                             uint32_t* __restrict__ tw, int64_t K, int64_t N, int gs) {
-  // columns n >= N pad the last strip: codes 8 (their zero point is 8 and
-  // their scale 1, see tile_scales / tile_zeros), so the weight is 0
-  const int64_t B = K / kTileK;
+                             uint32_t* __restrict__ tw, int64_t K, int64_t Kp, int64_t N, int gs, int Gp) {
+  // columns n >= N pad the last strip and rows k >= K (K % 128 != 0) pad the
+  // last block: their codes equal their zero point (8, or the per-channel
+  // zero point for padded rows of a per-channel layer; see tile_scales /
+  // tile_zeros for the padded scales 1 and zero points 8), so the weight is 0
+  const int64_t B = Kp / kTileK;
   const int64_t Np = (N + kTileN - 1) / kTileN * kTileN;
-  const int64_t total = K * Np / 8;
+  const int64_t total = Kp * Np / 8;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int j = (int)(idx & 3);
@@ -140,11 +142,17 @@ __global__ void tile_weights(const uint32_t* __restrict__ sw, const uint32_t* __
     const int64_t t = tb / B, b = tb - t * B;
     const int64_t n = kTileN * t + (l & 15);
     const int64_t k0 = kTileK * b + 32 * j + 8 * (l >> 4);
-    const int64_t g = k0 / gs;
     if (n >= N) {
       tw[idx] = 0x88888888u;
       continue;
     }
+    if (k0 >= K) {
+      // one group only (per-channel): the padded rows share its zero point
+      const uint32_t z = HAS_Z && Gp == 1 ? (sz[n / 8] >> (4 * (n & 7))) & 0xFu : 8u;
+      tw[idx] = z * 0x11111111u;
+      continue;
+    }
+    const int64_t g = k0 / gs;
     const uint16_t sbits = scales[g * N + n];
     uint32_t word = 0;
     if ((sbits & 0x7FFFu) == 0) {
@@ -169,16 +177,16 @@ __global__ void tile_weights(const uint32_t* __restrict__ sw, const uint32_t* __
 
 // One thread per column: walks the groups in order so that a zero scale can
 // take the previous group's stored scale.
-__global__ void tile_scales(const uint16_t* __restrict__ s, uint16_t* __restrict__ ts, int64_t N, int G,
+__global__ void tile_scales(const uint16_t* __restrict__ s, uint16_t* __restrict__ ts, int64_t N, int G, int Gp,
                             uint16_t one_bits) {
-  const int64_t Np = (N + kTileN - 1) / kTileN * kTileN;  // padded columns get scale 1
+  const int64_t Np = (N + kTileN - 1) / kTileN * kTileN;  // padded columns and groups get scale 1
   for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < Np; n += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = n / kTileN, c = n - t * kTileN;
     uint16_t prev = one_bits;
-    for (int g = 0; g < G; ++g) {
-      const uint16_t v = n < N ? s[(int64_t)g * N + n] : one_bits;
+    for (int g = 0; g < Gp; ++g) {
+      const uint16_t v = n < N && g < G ? s[(int64_t)g * N + n] : one_bits;
       const uint16_t out = (v & 0x7FFFu) == 0 ? prev : v;
-      ts[(t * G + g) * kTileN + c] = out;
+      ts[(t * Gp + g) * kTileN + c] = out;
       prev = out;
     }
   }
@@ -186,15 +194,15 @@ __global__ void tile_scales(const uint16_t* __restrict__ s, uint16_t* __restrict
 
 // Tiled zero word (t, g, w) is the standard zero word [g, 2t + w] (eight
 // padded columns, N % 16 == 8: zero points 8).
-__global__ void tile_zeros(const uint32_t* __restrict__ sz, uint32_t* __restrict__ tz, int64_t N, int G) {
+__global__ void tile_zeros(const uint32_t* __restrict__ sz, uint32_t* __restrict__ tz, int64_t N, int G, int Gp) {
   const int64_t T = (N + kTileN - 1) / kTileN;
-  const int64_t total = T * G * 2;
+  const int64_t total = T * Gp * 2;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int w = (int)(idx & 1);
     const int64_t tg = idx >> 1;
-    const int64_t t = tg / G, g = tg - t * G;
-    tz[idx] = 8 * (2 * t + w) < N ? sz[g * (N / 8) + 2 * t + w] : 0x88888888u;
+    const int64_t t = tg / Gp, g = tg - t * Gp;
+    tz[idx] = 8 * (2 * t + w) < N && g < G ? sz[g * (N / 8) + 2 * t + w] : 0x88888888u;
   }
 }
 
@@ -238,27 +246,27 @@ hipError_t launch_status_zero(int32_t* status, hipStream_t st) {
 hipError_t launch_tile(const Shape& s, const int32_t* std_w, const int32_t* std_z, const uint16_t* scales,
                        const int32_t* perm, int32_t* tiled_w, uint16_t* tiled_s, int32_t* tiled_z,
                        hipStream_t st) {
-  const int64_t total = s.K * s.Np / 8;
+  const int64_t total = s.Kp * s.Np / 8;
   const unsigned grid = grid_for(total, 256);
   const uint32_t* sw = reinterpret_cast<const uint32_t*>(std_w);
   const uint32_t* sz = reinterpret_cast<const uint32_t*>(std_z);
   uint32_t* tw = reinterpret_cast<uint32_t*>(tiled_w);
   if (s.has_z && s.has_perm)
-    tile_weights<true, true><<<grid, 256, 0, st>>>(sw, sz, scales, perm, tw, s.K, s.N, s.gs);
+    tile_weights<true, true><<<grid, 256, 0, st>>>(sw, sz, scales, perm, tw, s.K, s.Kp, s.N, s.gs, s.Gp);
   else if (s.has_z)
-    tile_weights<true, false><<<grid, 256, 0, st>>>(sw, sz, scales, perm, tw, s.K, s.N, s.gs);
+    tile_weights<true, false><<<grid, 256, 0, st>>>(sw, sz, scales, perm, tw, s.K, s.Kp, s.N, s.gs, s.Gp);
   else if (s.has_perm)
-    tile_weights<false, true><<<grid, 256, 0, st>>>(sw, sz, scales, perm, tw, s.K, s.N, s.gs);
+    tile_weights<false, true><<<grid, 256, 0, st>>>(sw, sz, scales, perm, tw, s.K, s.Kp, s.N, s.gs, s.Gp);
   else
-    tile_weights<false, false><<<grid, 256, 0, st>>>(sw, sz, scales, perm, tw, s.K, s.N, s.gs);
+    tile_weights<false, false><<<grid, 256, 0, st>>>(sw, sz, scales, perm, tw, s.K, s.Kp, s.N, s.gs, s.Gp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  tile_scales<<<grid_for(s.Np, 256), 256, 0, st>>>(scales, tiled_s, s.N, s.G, s.bf16 ? 0x3F80 : 0x3C00);
+  tile_scales<<<grid_for(s.Np, 256), 256, 0, st>>>(scales, tiled_s, s.N, s.G, s.Gp, s.bf16 ? 0x3F80 : 0x3C00);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (s.has_z) {
-    tile_zeros<<<grid_for(s.Np / kTileN * s.G * 2, 256), 256, 0, st>>>(sz, reinterpret_cast<uint32_t*>(tiled_z),
-                                                                       s.N, s.G);
+    tile_zeros<<<grid_for(s.Np / kTileN * s.Gp * 2, 256), 256, 0, st>>>(sz, reinterpret_cast<uint32_t*>(tiled_z),
+                                                                        s.N, s.G, s.Gp);
     e = hipGetLastError();
   }
   return e;

@@ -65,10 +65,12 @@ class W4A16Linear:
             std_z = torch.empty((G, N // 8), dtype=i32, device=d)
             A.w4_repack_awq(self.layer, qweight, qzeros, std_w, std_z, stream)
         T = (N + 15) // 16  # strips; a last half strip is padded
+        Kp = (K + 127) // 128 * 128  # rows padded to whole 128-row blocks
+        Gp = 1 if self.group_size == -1 else Kp // self.group_size
         tiled = {
-            "qweight": torch.empty((K * T * 2,), dtype=i32, device=d),
-            "scales": torch.empty((T, G, 16), dtype=_TORCH_DTYPE[self.dtype], device=d),
-            "qzeros": torch.empty((T, G, 2), dtype=i32, device=d) if self.has_zero_points else None,
+            "qweight": torch.empty((Kp * T * 2,), dtype=i32, device=d),
+            "scales": torch.empty((T, Gp, 16), dtype=_TORCH_DTYPE[self.dtype], device=d),
+            "qzeros": torch.empty((T, Gp, 2), dtype=i32, device=d) if self.has_zero_points else None,
             "perm": torch.empty((K,), dtype=i32, device=d) if self.has_g_idx else None,
         }
         status = torch.empty((1,), dtype=i32, device=d) if self.has_g_idx else None
@@ -128,10 +130,13 @@ class W4A16Linear:
 class W4A16MoELinear:
     """The grouped (mixture-of-experts) layer: E experts of one shape, each
     repacked into its slice of stacked tile buffers, applied in one launch to
-    rows grouped by expert (w4a16_moe_linear).  Act-order is not supported."""
+    rows grouped by expert (w4a16_moe_linear).  Act-order and K % 128 != 0
+    are not supported."""
 
     def __init__(self, num_experts: int, K: int, N: int, group_size: int = 128, has_zero_points: bool = True,
                  dtype: str = "fp16", fmt: str = "awq", device="cuda"):
+        if K % 128 != 0:
+            raise A.W4Error("W4A16MoELinear", A.W4_ERR_UNSUPPORTED, "the grouped launch needs K % 128 == 0")
         self.E = int(num_experts)
         self.experts = [W4A16Linear(K, N, group_size, has_zero_points, False, dtype, fmt, device=device)
                         for _ in range(self.E)]
