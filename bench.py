@@ -488,7 +488,8 @@ def cpu_baseline(cases, seconds):
         if spent >= seconds:
             break
     return {"value": round(wbytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(done)} whole-layer oracle calls: " + " ".join(done), "seconds": round(spent, 2)}
+            "sample": f"{len(done)} whole-layer oracle calls cycling through the cases "
+                      + " ".join(dict.fromkeys(done)), "seconds": round(spent, 2)}
 
 
 if __name__ == "__main__":
