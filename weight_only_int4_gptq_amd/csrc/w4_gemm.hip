@@ -856,14 +856,15 @@ inline size_t skinny_lds_bytes(int mt, int nb, int kw, bool xl, int64_t M, int64
 }
 
 // Ring depth of a skinny configuration (from timing sweeps): double
-// buffering with LDS activations, where deeper rings measured slower; three
-// or four blocks in flight when the activations come from registers.
-template <int MT, int NB, bool XL, bool HP>
+// buffering with LDS activations, where deeper rings measured slower; with
+// the activations in registers, six blocks in flight for one strip and eight
+// waves, three for sixteen waves or two strips.
+template <int MT, int NB, int KW, bool XL>
 constexpr int skinny_depth() {
-  return XL ? 2 : (MT * NB == 1 ? 4 : (MT * NB == 2 ? 3 : 2));
+  return XL ? 2 : (MT * NB == 1 ? (KW >= 16 ? 3 : 6) : (MT * NB == 2 ? 3 : 2));
 }
 
-template <int MT, int NB, int KW, int GM, bool BF16, bool HZ, bool HP, bool XL, int D = skinny_depth<MT, NB, XL, HP>()>
+template <int MT, int NB, int KW, int GM, bool BF16, bool HZ, bool HP, bool XL, int D = skinny_depth<MT, NB, KW, XL>()>
 hipError_t run_skinny(const Args& a, hipStream_t st) {
   const int64_t T = (a.N + kTileN - 1) / kTileN;
   if (T % NB != 0) return hipErrorInvalidValue;
@@ -1060,8 +1061,11 @@ GemmPlan plan_gemm(const Shape& s, int64_t M) {
     p.wide = idx;
   } else if (M <= 16) {
     // activations from registers; two strips per workgroup share them
-    // (halving the activation traffic) unless N is small and K long
-    if (T % 2 == 0 && (T >= 512 || s.K <= 4096)) {
+    // (halving the activation traffic) unless N is small: then one strip
+    // per workgroup, sixteen waves for short K, eight for long K
+    if (T <= 256 && s.K <= 4096) {
+      p = GemmPlan{GemmKind::kSkinny, 1, 1, 16, false, "w4_skinny_k16"};
+    } else if (T % 2 == 0 && (T >= 512 || s.K <= 4096)) {
       p = s.K >= 8192 ? GemmPlan{GemmKind::kSkinny, 1, 2, 8, false, "w4_skinny_n2_k8"}
                       : GemmPlan{GemmKind::kSkinny, 1, 2, 16, false, "w4_skinny_n2_k16"};
     } else {
@@ -1164,7 +1168,7 @@ hipError_t launch_gemm(const Shape& s0, int64_t M, const void* x, const int32_t*
   }
   if (p.xl) return p.kw == 16 ? pick_flags<1, 1, 16, true>(sk, a, st) : pick_flags<1, 1, 8, true>(sk, a, st);
   if (p.nb == 2) return p.kw == 16 ? pick_flags<1, 2, 16, false>(sk, a, st) : pick_flags<1, 2, 8, false>(sk, a, st);
-  return pick_flags<1, 1, 8, false>(sk, a, st);
+  return p.kw == 16 ? pick_flags<1, 1, 16, false>(sk, a, st) : pick_flags<1, 1, 8, false>(sk, a, st);
 }
 
 GemmPlan plan_moe(const Shape& s, int64_t max_rows, int experts) {
