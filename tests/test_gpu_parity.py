@@ -396,7 +396,8 @@ def test_linear_full_size_sampled(W, c, M):
 
 # (M, N) pairs that select each wide tile of the kernel table (128x128,
 # 64x256, 64x128, 32x128, the split-K 64x128 and 32x128 launches of M <= 64,
-# and the one-wave 16x16 and 16x32 tiles of M <= 16 on wide layers);
+# and the 16-row tiles of M <= 16 on wide layers: four waves of one strip up
+# to 1024 strips, two waves beyond, and an odd strip count);
 # K = 1152 is nine 128-row blocks, so every pipeline depth runs full trips and
 # a partial tail, and a 4-way split gives uneven K ranges (2, 2, 2, 3).
 WIDE_TILE_SHAPES = [(1024, 16384), (256, 32768), (64, 32768), (32, 32768), (40, 8192), (24, 8192), (200, 8192),

@@ -963,12 +963,14 @@ constexpr WideChoice kWide[] = {
     {2, 2, 4, 8, 0, "w4_wide_32x128"},
     {2, 2, 2, 8, 0, "w4_wide_32x64"},
     {2, 1, 2, 8, 0, "w4_wide_32x32"},
-    // 16-row tiles, one wave per workgroup: M <= 16 on wide layers (below)
+    // 16-row tiles: M <= 16 on wide layers and grouped (MoE) launches (below)
     {1, 1, 1, 8, 0, "w4_wide_16x16"},
     {1, 2, 1, 8, 0, "w4_wide_16x32"},
+    {1, 1, 4, 8, 0, "w4_wide_16x64_w4"},
+    {1, 1, 2, 6, 0, "w4_wide_16x32_w2"},
 };
 constexpr int kNumWide = 6;  // entries searched for M > 16
-constexpr int kWide16x16 = 6, kWide16x32 = 7;
+constexpr int kWide16x16 = 6, kWide16x32 = 7, kWide16x64w4 = 8, kWide16x32w2 = 9;
 
 hipError_t wide_dispatch(int idx, const Shape& s, const Args& a, const uint16_t* x, hipStream_t st) {
   switch (idx) {
@@ -979,7 +981,9 @@ hipError_t wide_dispatch(int idx, const Shape& s, const Args& a, const uint16_t*
     case 4: return wide_flags<2, 2, 2, 8>(s, a, x, st);
     case 5: return wide_flags<2, 1, 2, 8>(s, a, x, st);
     case 6: return wide_flags<1, 1, 1, 8>(s, a, x, st);
-    default: return wide_flags<1, 2, 1, 8>(s, a, x, st);
+    case 7: return wide_flags<1, 2, 1, 8>(s, a, x, st);
+    case 8: return wide_flags<1, 1, 4, 8>(s, a, x, st);
+    default: return wide_flags<1, 1, 2, 6>(s, a, x, st);
   }
 }
 
@@ -1053,9 +1057,11 @@ GemmPlan plan_gemm(const Shape& s, int64_t M) {
     p = k16 ? GemmPlan{GemmKind::kSkinny, 1, 1, 16, true, "w4_skinny_lds_k16"}
             : GemmPlan{GemmKind::kSkinny, 1, 1, 8, true, "w4_skinny_lds_k8"};
   } else if (M <= 16 && T >= 768) {
-    // many strips (N >= 12288): one wave per workgroup walks all of K with
-    // the activation tile in LDS, which measured faster than splitting K
-    const int idx = T <= 1024 ? kWide16x16 : kWide16x32;
+    // many strips (N >= 12288): every wave walks all of K for one strip with
+    // the activation tile in LDS shared by the workgroup's waves (four for
+    // up to 1024 strips, else two with a six-deep pipeline), which measured
+    // faster than splitting K
+    const int idx = T <= 1024 ? kWide16x64w4 : kWide16x32w2;
     const WideChoice& w = kWide[idx];
     p = GemmPlan{GemmKind::kWide, w.mt, w.ns, w.wn, false, w.name};
     p.wide = idx;
