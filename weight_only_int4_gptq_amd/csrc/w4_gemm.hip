@@ -365,30 +365,51 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
     // written).
     const int rows = (int)((M - m0) < kXlRows ? (M - m0) : kXlRows);
     const int64_t K8 = K / 8;
-    for (int64_t k8 = threadIdx.x; k8 < K8; k8 += 64 * KW) {
-      u4 val[kXlRows];
-      if constexpr (!HAS_PERM) {
+    if constexpr (!HAS_PERM) {
+      for (int64_t k8 = threadIdx.x; k8 < K8; k8 += 64 * KW) {
+        u4 val[kXlRows];
 #pragma unroll
         for (int r = 0; r < kXlRows; ++r)
           if (r < rows) val[r] = *reinterpret_cast<const u4*>(x + (m0 + r) * K + 8 * k8);
-      } else {
-        const int4 p0 = *reinterpret_cast<const int4*>(perm + 8 * k8);
-        const int4 p1 = *reinterpret_cast<const int4*>(perm + 8 * k8 + 4);
-        const uint32_t idx[8] = {(uint32_t)p0.x, (uint32_t)p0.y, (uint32_t)p0.z, (uint32_t)p0.w,
+#pragma unroll
+        for (int r = 0; r < kXlRows; ++r)
+          if (r < rows) *reinterpret_cast<u4*>(xlds + r * (K + kXPad) + 8 * k8) = val[r];
+      }
+    } else {
+      // act-order: each thread takes two chunk columns per trip, loading the
+      // perm entries of both before any gather, so the dependent loads cost
+      // two memory latencies per pair rather than per chunk column (the
+      // second chunk repeats the first past the end of K: same values to
+      // the same place)
+      const int64_t step = 64 * KW;
+      for (int64_t k8 = threadIdx.x; k8 < K8; k8 += 2 * step) {
+        const int64_t kc[2] = {k8, k8 + step < K8 ? k8 + step : k8};
+        uint32_t idx[2][8];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int4 p0 = *reinterpret_cast<const int4*>(perm + 8 * kc[c]);
+          const int4 p1 = *reinterpret_cast<const int4*>(perm + 8 * kc[c] + 4);
+          const uint32_t q[8] = {(uint32_t)p0.x, (uint32_t)p0.y, (uint32_t)p0.z, (uint32_t)p0.w,
                                  (uint32_t)p1.x, (uint32_t)p1.y, (uint32_t)p1.z, (uint32_t)p1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) idx[c][e] = q[e] < (uint32_t)K ? q[e] : 0u;
+        }
 #pragma unroll
         for (int r = 0; r < kXlRows; ++r) {
           if (r >= rows) continue;
           const uint16_t* src = x + (m0 + r) * K;
-          uint32_t h[8];
+          uint32_t h[2][8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) h[e] = src[idx[e] < (uint32_t)K ? idx[e] : 0u];
-          val[r] = u4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[c][e] = src[idx[c][e]];
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            *reinterpret_cast<u4*>(xlds + r * (K + kXPad) + 8 * kc[c]) =
+                u4{h[c][0] | (h[c][1] << 16), h[c][2] | (h[c][3] << 16), h[c][4] | (h[c][5] << 16),
+                   h[c][6] | (h[c][7] << 16)};
         }
       }
-#pragma unroll
-      for (int r = 0; r < kXlRows; ++r)
-        if (r < rows) *reinterpret_cast<u4*>(xlds + r * (K + kXPad) + 8 * k8) = val[r];
     }
     __syncthreads();
   }
