@@ -674,6 +674,13 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
 #pragma unroll
     for (int j = 0; j < NS; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
   const u4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  // fp16 with several groups: the B operand can be (q - z) s rounded once
+  // to fp16, so the accumulators hold y directly.  That costs 4 packed
+  // multiplies per step and strip, the per-period rescale 4 MT multiplies
+  // per period and strip, so it is used where MT exceeds the steps per
+  // period.  bf16 keeps the exact (128 + q) operand (a bf16 product would
+  // round away too much), and per-channel layers scale once at the end.
+  constexpr bool PRE = !BF16 && GM != GM_CH && MT > SP;
   float s_prev[NS];
 #pragma unroll
   for (int nt = 0; nt < NS; ++nt) s_prev[nt] = 1.f;
@@ -685,12 +692,17 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
     for (int p = 0; p < NP; ++p) {
       uint32_t n1[NS], n2[NS];
       float nzz[NS];
+      h2 s2[NS];
 #pragma unroll
       for (int nt = 0; nt < NS; ++nt) {
         const uint32_t z = HAS_Z ? (r.z[nt][p] >> zshift) & 0xFu : 8u;
         n1[nt] = nz1024_bits(z);
         n2[nt] = nz64_bits(z);
         nzz[nt] = -(128.0f + (float)z);
+        if constexpr (PRE) {
+          s2[nt] = bit_as<h2>((uint32_t)r.s[nt][p] * 0x10001u);
+          continue;
+        }
         const float s_cur = act_to_f32<BF16>(r.s[nt][p]);
         if constexpr (GM != GM_CH) {
           const float ratio = s_prev[nt] * __builtin_amdgcn_rcpf(s_cur);
@@ -723,6 +735,9 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
             bq = dq_bf16(r.w[nt][j], nm);
           else
             bq = dq_f16(r.w[nt][j], n1[nt], n2[nt], nm);
+          if constexpr (PRE)
+            bq = u4{bit_as<uint32_t>(bit_as<h2>(bq.x) * s2[nt]), bit_as<uint32_t>(bit_as<h2>(bq.y) * s2[nt]),
+                    bit_as<uint32_t>(bit_as<h2>(bq.z) * s2[nt]), bit_as<uint32_t>(bit_as<h2>(bq.w) * s2[nt])};
 #pragma unroll
           for (int i = 0; i < MT; ++i) acc[i][nt] = mfma<BF16>(a[i], bq, acc[i][nt]);
         }
