@@ -1215,12 +1215,14 @@ hipError_t launch_gemm(const Shape& s0, int64_t M, const void* x, const int32_t*
 
 GemmPlan plan_moe(const Shape& s, int64_t max_rows, int experts) {
   // grouped launch of the wide kernel (no split-K): 16-row tiles for up to
-  // 16 rows per expert, else the largest tile not taller than the rows that
-  // still gives >= 256 workgroups over all experts
+  // 16 rows per expert (two waves of one strip each once there are >= 1024
+  // strips over all experts, else one wave of one strip), else the largest
+  // tile not taller than the rows that still gives >= 256 workgroups over
+  // all experts
   const int64_t T = s.Np / kTileN;
   int idx = kNumWide - 1;
   if (max_rows <= 16) {
-    idx = T * experts >= 1024 ? kWide16x32 : kWide16x16;
+    idx = T * experts >= 1024 ? kWide16x32w2 : kWide16x16;
   } else {
     for (int i = 0; i < kNumWide; ++i) {
       const WideChoice& w = kWide[i];
