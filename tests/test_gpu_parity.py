@@ -445,18 +445,22 @@ def test_linear_wide_tiles_sampled(W, v):
 # HIP graph capture: replays match the eager launch bit for bit
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M", [1, 16, 40, 300])
-def test_linear_hip_graph_replays_match_eager(W, M):
+@pytest.mark.parametrize("M,K,gs,act", [(1, 1152, 128, True), (16, 1152, 128, True), (40, 1152, 128, True),
+                                        (300, 1152, 128, True), (1, 1120, 32, False), (40, 1120, 32, False),
+                                        (300, 1120, 32, False)])
+def test_linear_hip_graph_replays_match_eager(W, M, K, gs, act):
+    # act-order (gather into the workspace) and K tails (zero-padded copy
+    # into the workspace) inside a captured graph
     import torch
-    K, N, gs = 1152, 4096, 128
+    N = 4096
     G = K // gs
-    rng = seeded(606, M)
+    rng = seeded(606, M, K)
     qweight = random_words(rng, (K // 8, N))
     qzeros = random_words(rng, (G, N // 8))
     scales = uniform_scales(rng, (G, N), 0.002, 0.02, "fp16")
-    g_idx = actorder_gidx(rng, K, gs)
-    Lyr = _prepare(W, "std", K, N, gs, True, True, "fp16", qweight, qzeros, scales, g_idx)
-    say(f"graph M={M} kernel={Lyr.kernel_name(M)}")
+    g_idx = actorder_gidx(rng, K, gs) if act else None
+    Lyr = _prepare(W, "std", K, N, gs, True, act, "fp16", qweight, qzeros, scales, g_idx)
+    say(f"graph M={M} K={K} g={gs} act={act} kernel={Lyr.kernel_name(M)}")
     x = to_dev(normal_acts(seeded(607, M), (M, K), "fp16"))
     t = Lyr.tiled
     ws_b = W.w4_workspace_size(Lyr.layer, M)
