@@ -222,21 +222,20 @@ struct BlockRegs {
 // purpose: an exec-masked load region here let the compiler fold the row
 // mask into the loop's active-lane mask, so the next block's B operands were
 // built for the masked lanes only.
-template <int MT, int NB, int GM, bool HAS_Z, bool HAS_PERM, bool XL>
+template <int MT, int NB, int GM, bool HAS_Z, bool XL>
 struct LaneView {
   static constexpr int NP = Groups<GM>::kPeriods;
   const u4* w[NB];            // tiled words of strip s at block 0 (lane's 16 bytes)
   const uint16_t* sc[NB];     // scale of column c of strip s, group 0
   const uint32_t* zs[NB];     // zero word holding column c of strip s, group 0
-  const uint16_t* xr[MT];     // x row of tile i (+ 8 * quad without act-order)
-  const int32_t* pm;          // perm + 8 * quad
+  const uint16_t* xr[MT];     // x row of tile i + 8 * quad
   const uint16_t* xl;         // XL: LDS row of this lane + 8 * quad
   bool row_ok[MT];            // row of tile i is < M
   int64_t nblk;
 
   __device__ __forceinline__ void init(const uint16_t* x, const u4* qw, const uint16_t* scl, const uint32_t* zsp,
-                                       const int32_t* perm, const uint16_t* xlds, int64_t t0, int64_t m0, int64_t M,
-                                       int64_t K, int G, int lane) {
+                                       const uint16_t* xlds, int64_t t0, int64_t m0, int64_t M, int64_t K, int G,
+                                       int lane) {
     const int c = lane & 15, quad = lane >> 4;
     nblk = K / kTileK;
 #pragma unroll
@@ -250,9 +249,8 @@ struct LaneView {
       int64_t m = m0 + 16 * i + c;
       row_ok[i] = m < M;
       m = m < M ? m : M - 1;
-      xr[i] = x + m * K + (HAS_PERM ? 0 : 8 * quad);
+      xr[i] = x + m * K + 8 * quad;
     }
-    pm = perm + 8 * quad;
     // LDS rows >= M are never staged; read row 0 instead
     xl = xlds + (row_ok[0] ? c : 0) * (K + kXPad) + 8 * quad;
   }
@@ -262,23 +260,8 @@ struct LaneView {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = kb * kTileK + 32 * j;
-      if constexpr (!HAS_PERM) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i) a[i][j] = *reinterpret_cast<const u4*>(xr[i] + k);
-      } else {
-        const int4 p0 = *reinterpret_cast<const int4*>(pm + k);
-        const int4 p1 = *reinterpret_cast<const int4*>(pm + k + 4);
-        const uint32_t idx[8] = {(uint32_t)p0.x, (uint32_t)p0.y, (uint32_t)p0.z, (uint32_t)p0.w,
-                                 (uint32_t)p1.x, (uint32_t)p1.y, (uint32_t)p1.z, (uint32_t)p1.w};
-        const uint32_t Ku = (uint32_t)(nblk * kTileK);
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          uint32_t h[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) h[e] = xr[i][idx[e] < Ku ? idx[e] : 0u];
-          a[i][j] = u4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-        }
-      }
+      for (int i = 0; i < MT; ++i) a[i][j] = *reinterpret_cast<const u4*>(xr[i] + k);
     }
   }
 
@@ -305,11 +288,10 @@ struct LaneView {
 };
 
 // Skinny kernel: see the header comment.  XL: activations staged in LDS.
-template <int MT, int NB, int KW, int GM, bool BF16, bool HAS_Z, bool HAS_PERM, bool XL, int D>
+template <int MT, int NB, int KW, int GM, bool BF16, bool HAS_Z, bool XL, int D>
 __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restrict__ x, const u4* __restrict__ qw,
                                                         const uint16_t* __restrict__ sc,
                                                         const uint32_t* __restrict__ zs,
-                                                        const int32_t* __restrict__ perm,
                                                         const uint16_t* __restrict__ bias,
                                                         uint16_t* __restrict__ y, int64_t M, int64_t K, int64_t N,
                                                         int G) {
@@ -325,8 +307,8 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
   const int64_t t0 = (int64_t)blockIdx.x * NB;
   const int64_t m0 = (int64_t)blockIdx.y * 16 * MT;
 
-  LaneView<MT, NB, GM, HAS_Z, HAS_PERM, XL> v;
-  v.init(x, qw, sc, zs, perm, xlds, t0, m0, M, K, G, lane);
+  LaneView<MT, NB, GM, HAS_Z, XL> v;
+  v.init(x, qw, sc, zs, xlds, t0, m0, M, K, G, lane);
   const int nblk = (int)v.nblk;
   // wave w owns the contiguous blocks [lo, hi) of K (wave-uniform bounds)
   const int lo = __builtin_amdgcn_readfirstlane((int)(((int64_t)nblk * wave) / KW));
@@ -365,51 +347,14 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
     // written).
     const int rows = (int)((M - m0) < kXlRows ? (M - m0) : kXlRows);
     const int64_t K8 = K / 8;
-    if constexpr (!HAS_PERM) {
-      for (int64_t k8 = threadIdx.x; k8 < K8; k8 += 64 * KW) {
-        u4 val[kXlRows];
+    for (int64_t k8 = threadIdx.x; k8 < K8; k8 += 64 * KW) {
+      u4 val[kXlRows];
 #pragma unroll
-        for (int r = 0; r < kXlRows; ++r)
-          if (r < rows) val[r] = *reinterpret_cast<const u4*>(x + (m0 + r) * K + 8 * k8);
+      for (int r = 0; r < kXlRows; ++r)
+        if (r < rows) val[r] = *reinterpret_cast<const u4*>(x + (m0 + r) * K + 8 * k8);
 #pragma unroll
-        for (int r = 0; r < kXlRows; ++r)
-          if (r < rows) *reinterpret_cast<u4*>(xlds + r * (K + kXPad) + 8 * k8) = val[r];
-      }
-    } else {
-      // act-order: each thread takes two chunk columns per trip, loading the
-      // perm entries of both before any gather, so the dependent loads cost
-      // two memory latencies per pair rather than per chunk column (the
-      // second chunk repeats the first past the end of K: same values to
-      // the same place)
-      const int64_t step = 64 * KW;
-      for (int64_t k8 = threadIdx.x; k8 < K8; k8 += 2 * step) {
-        const int64_t kc[2] = {k8, k8 + step < K8 ? k8 + step : k8};
-        uint32_t idx[2][8];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int4 p0 = *reinterpret_cast<const int4*>(perm + 8 * kc[c]);
-          const int4 p1 = *reinterpret_cast<const int4*>(perm + 8 * kc[c] + 4);
-          const uint32_t q[8] = {(uint32_t)p0.x, (uint32_t)p0.y, (uint32_t)p0.z, (uint32_t)p0.w,
-                                 (uint32_t)p1.x, (uint32_t)p1.y, (uint32_t)p1.z, (uint32_t)p1.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) idx[c][e] = q[e] < (uint32_t)K ? q[e] : 0u;
-        }
-#pragma unroll
-        for (int r = 0; r < kXlRows; ++r) {
-          if (r >= rows) continue;
-          const uint16_t* src = x + (m0 + r) * K;
-          uint32_t h[2][8];
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) h[c][e] = src[idx[c][e]];
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-            *reinterpret_cast<u4*>(xlds + r * (K + kXPad) + 8 * kc[c]) =
-                u4{h[c][0] | (h[c][1] << 16), h[c][2] | (h[c][3] << 16), h[c][4] | (h[c][5] << 16),
-                   h[c][6] | (h[c][7] << 16)};
-        }
-      }
+      for (int r = 0; r < kXlRows; ++r)
+        if (r < rows) *reinterpret_cast<u4*>(xlds + r * (K + kXPad) + 8 * k8) = val[r];
     }
     __syncthreads();
   }
@@ -851,7 +796,7 @@ __global__ void pad_columns(const uint4* __restrict__ x, uint4* __restrict__ xp,
   }
 }
 
-// x_perm[m][k'] = x[m][perm[k']] for the act-order wide path (perm entries
+// x_perm[m][k'] = x[m][perm[k']]: the act-order activations of every path (perm entries
 // outside [0, K) read column 0).
 __global__ void gather_columns(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
                                uint16_t* __restrict__ xp, int64_t M, int64_t K) {
@@ -900,7 +845,7 @@ constexpr int skinny_depth() {
   return XL ? 2 : (MT * NB == 1 ? (KW >= 16 ? 3 : 6) : (MT * NB == 2 ? 3 : 2));
 }
 
-template <int MT, int NB, int KW, int GM, bool BF16, bool HZ, bool HP, bool XL, int D = skinny_depth<MT, NB, KW, XL>()>
+template <int MT, int NB, int KW, int GM, bool BF16, bool HZ, bool XL, int D = skinny_depth<MT, NB, KW, XL>()>
 hipError_t run_skinny(const Args& a, hipStream_t st) {
   const int64_t T = (a.N + kTileN - 1) / kTileN;
   if (T % NB != 0) return hipErrorInvalidValue;
@@ -917,14 +862,14 @@ hipError_t run_skinny(const Args& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
     if (bit == 0 || (allowed.load(std::memory_order_relaxed) & bit) == 0) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_skinny<MT, NB, KW, GM, BF16, HZ, HP, XL, D>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_skinny<MT, NB, KW, GM, BF16, HZ, XL, D>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxSkinnyLds);
       if (e != hipSuccess) return e;
       allowed.fetch_or(bit, std::memory_order_relaxed);
     }
   }
-  gemm_skinny<MT, NB, KW, GM, BF16, HZ, HP, XL, D><<<grid, 64 * KW, lds, st>>>(
-      a.x, a.qw, a.sc, a.zs, a.perm, a.bias, a.y, a.M, a.K, a.N, a.G);
+  gemm_skinny<MT, NB, KW, GM, BF16, HZ, XL, D><<<grid, 64 * KW, lds, st>>>(
+      a.x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N, a.G);
   return hipGetLastError();
 }
 
@@ -1024,12 +969,12 @@ hipError_t wide_dispatch(int idx, const Shape& s, const Args& a, const uint16_t*
 }
 
 // Workspace of a call: first the activations the kernels read instead of x
-// (gathered through perm with act-order on every path but the LDS-staged
-// skinny kernel; or padded to whole 128-row blocks when K % 128 != 0; the
-// two never coincide), then the split-K partials.
+// (gathered through perm with act-order, on every path; or padded to whole
+// 128-row blocks when K % 128 != 0; the two never coincide), then the
+// split-K partials.
 inline size_t front_bytes(const Shape& s, const GemmPlan& p, int64_t M) {
   size_t b = 0;
-  if (s.has_perm && !p.xl) b = (size_t)M * (size_t)s.K * sizeof(uint16_t);
+  if (s.has_perm) b = (size_t)M * (size_t)s.K * sizeof(uint16_t);
   else if (s.K != s.Kp) b = (size_t)M * (size_t)s.Kp * sizeof(uint16_t);
   return (b + 255) / 256 * 256;
 }
@@ -1050,29 +995,22 @@ hipError_t launch_wide(const Shape& s, const GemmPlan& p, const Args& a0, void* 
   return wide_dispatch(p.wide, s, a, x, st);
 }
 
-template <int MT, int NB, int KW, bool XL, bool BF16, bool HZ, bool HP>
+template <int MT, int NB, int KW, bool XL, bool BF16, bool HZ>
 hipError_t pick_gm(const Args& a, hipStream_t st) {
   switch (group_mode(a.gs, a.K)) {
-    case GM_32: return run_skinny<MT, NB, KW, GM_32, BF16, HZ, HP, XL>(a, st);
-    case GM_64: return run_skinny<MT, NB, KW, GM_64, BF16, HZ, HP, XL>(a, st);
-    case GM_128: return run_skinny<MT, NB, KW, GM_128, BF16, HZ, HP, XL>(a, st);
-    default: return run_skinny<MT, NB, KW, GM_CH, BF16, HZ, HP, XL>(a, st);
+    case GM_32: return run_skinny<MT, NB, KW, GM_32, BF16, HZ, XL>(a, st);
+    case GM_64: return run_skinny<MT, NB, KW, GM_64, BF16, HZ, XL>(a, st);
+    case GM_128: return run_skinny<MT, NB, KW, GM_128, BF16, HZ, XL>(a, st);
+    default: return run_skinny<MT, NB, KW, GM_CH, BF16, HZ, XL>(a, st);
   }
 }
 
+// (act-order activations arrive gathered: the skinny kernels never see perm)
 template <int MT, int NB, int KW, bool XL>
 hipError_t pick_flags(const Shape& s, const Args& a, hipStream_t st) {
-  // act-order reaches the kernels only on the LDS-staged path (which gathers
-  // while staging); the register path receives pre-gathered activations
-  const bool hp = XL && s.has_perm;
-  if (s.bf16) {
-    if (s.has_z)
-      return hp ? pick_gm<MT, NB, KW, XL, true, true, XL>(a, st) : pick_gm<MT, NB, KW, XL, true, true, false>(a, st);
-    return hp ? pick_gm<MT, NB, KW, XL, true, false, XL>(a, st) : pick_gm<MT, NB, KW, XL, true, false, false>(a, st);
-  }
-  if (s.has_z)
-    return hp ? pick_gm<MT, NB, KW, XL, false, true, XL>(a, st) : pick_gm<MT, NB, KW, XL, false, true, false>(a, st);
-  return hp ? pick_gm<MT, NB, KW, XL, false, false, XL>(a, st) : pick_gm<MT, NB, KW, XL, false, false, false>(a, st);
+  if (s.bf16)
+    return s.has_z ? pick_gm<MT, NB, KW, XL, true, true>(a, st) : pick_gm<MT, NB, KW, XL, true, false>(a, st);
+  return s.has_z ? pick_gm<MT, NB, KW, XL, false, true>(a, st) : pick_gm<MT, NB, KW, XL, false, false>(a, st);
 }
 
 }  // namespace
@@ -1199,7 +1137,7 @@ hipError_t launch_gemm(const Shape& s0, int64_t M, const void* x, const int32_t*
   }
   if (p.kind == GemmKind::kWide) return launch_wide(s, p, a, ws, front, st);
   Shape sk = s;
-  if (s.has_perm && !p.xl) {
+  if (s.has_perm) {
     // gather x[:, perm] into the workspace, then run without act-order
     uint16_t* xp = static_cast<uint16_t*>(ws);
     const hipError_t e = launch_gather(a.x, a.perm, xp, a.M, a.K, st);
