@@ -1,23 +1,30 @@
 """Benchmark of the W4A16 linear layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode|mid|prefill|actorder|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--config all|decode|tiny|mid|prefill|actorder|moe] [--compare] [--group-size G]
 
 A step is one forward pass of the hot path over every (shape, M) case of the
-chosen workload: for each case one w4a16_linear call (host validation, kernel
-selection, fused dequantize + GEMM, epilogue) on activations and weights that
-are already resident in HBM.  The timed launches are recorded into a HIP
-graph and replayed (as a serving loop would), so the ~5 us host cost of a
-Python call does not starve the GPU between short decode kernels; --eager
-times direct launches instead.  The one-time repacks (AWQ -> standard ->
-tile layout) are timed separately and reported under "repack".
+decode workload (7B-class layers, M = 1, 4, 16): for each case one
+w4a16_linear call (host validation, kernel selection, fused dequantize +
+GEMM, epilogue) on activations and weights already resident in HBM.  K steps
+are recorded into a HIP graph; one untimed replay uploads it and one replay
+is timed (a serving loop replays graphs the same way, so the ~5 us host cost
+of a Python call does not starve the GPU between short decode kernels;
+--eager times direct launches instead).  ``value`` is packed-weight GB/s of
+that step.
+
+With ``--config all`` (the default) the line also carries one block per
+workload (decode, tiny, mid-batch, prefill, act-order), so the metric is
+covered over M = 1..8192: each case is timed alone as the median of five
+replays of a graph of back-to-back launches, and each block reports its
+roofline (HBM-bound cases against 8 TB/s on algorithmic bytes, MFMA-bound
+cases against the dense fp16/bf16 peak on 2 M K N flops).
 
 Weight buffers are rotated over enough copies that every launch reads its
-weights from HBM (the working set exceeds the 256 MB Infinity Cache).
-
-Prints ONE JSON line.  ``value`` is packed-weight GB/s of the whole step
-(sum of K*N/2 over the cases / step time); ``roofline`` is for the GEMM
-kernel with achieved = algorithmic bytes per launch / HIP-event launch time;
-``cpu_baseline`` times the CPU oracle on a bounded sample of the workload.
+weights from HBM (the working set exceeds the 256 MB Infinity Cache).  The
+one-time repacks (AWQ -> standard -> tile layout) are timed separately.
+``cpu_baseline`` times the CPU oracle's three phases (unpack + order fix +
+standard repack, float64 dequantization, float64 matmul) on a bounded sample.
 """
 from __future__ import annotations
 
@@ -25,6 +32,8 @@ import argparse
 import json
 import math
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -36,21 +45,25 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A16 GEMM TFLOPS + packed-weight HBM GB/s (% roofline), M=1..8192"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+RIDGE = MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
 ROTATE_BYTES = 512 << 20       # working set per shape, > 256 MB MALL
 COPY_PROBE_BYTES = 256 << 20   # plain device copy used to calibrate byte counters
+REPLAYS = 5                    # per-case timing: median of this many graph replays
+WORKLOADS = ("decode", "tiny", "mid", "prefill", "actorder")
+CFG_ID = {"tiny": 1, "decode": 2, "mid": 3, "prefill": 4, "actorder": 5}
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", default="decode", choices=["tiny", "decode", "mid", "prefill", "actorder", "moe"])
-    p.add_argument("--reps", type=int, default=0, help="launches per case for the per-kernel timing (0 = auto)")
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", default="all", choices=["all", *WORKLOADS, "moe"])
+    p.add_argument("--reps", type=int, default=0, help="launches per case graph (0 = auto)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--group-size", type=int, default=0, choices=[0, 32, 64, 128, -1],
-                   help="run the workload's shapes with this group size instead (0 = the workload's own)")
+                   help="run the workloads' shapes with this group size instead (0 = their own)")
     p.add_argument("--compare", action="store_true",
                    help="also time the unfused path (dense dequantization kernel, then torch.matmul) per case")
     p.add_argument("--eager", action="store_true",
@@ -87,8 +100,8 @@ def _to_dev(torch, a):
 
 
 def case_bytes(c, M):
-    """Algorithmic HBM bytes of one launch: packed weights + scales + zeros +
-    x + y (+ perm)."""
+    """(packed-weight bytes, algorithmic HBM bytes) of one launch: packed
+    weights + scales + zeros + x + y (+ perm)."""
     w = c.K * c.N // 2
     s = c.G * c.N * 2
     z = c.G * c.N // 2 if c.has_zeros else 0
@@ -96,6 +109,201 @@ def case_bytes(c, M):
     y = M * c.N * 2
     p = c.K * 4 if c.has_gidx else 0
     return w, w + s + z + x + y + p
+
+
+def roofline_of(cases):
+    """Roofline objects of a set of timed cases, one per bound: a case whose
+    flop per algorithmic byte is below the ridge is HBM-bound, else
+    MFMA-bound.  achieved = algorithmic bytes (flops) of the cases / the sum
+    of their per-launch times."""
+    out = []
+    for bound in ("hbm", "mfma"):
+        sel = [p for p in cases if (p["_flops"] / p["_tb"] < RIDGE) == (bound == "hbm")]
+        if not sel:
+            continue
+        us = sum(p["_us"] for p in sel)
+        if bound == "hbm":
+            ach = sum(p["_tb"] for p in sel) / (us * 1e-6) / 1e9
+            r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+        else:
+            ach = sum(p["_flops"] for p in sel) / (us * 1e-6) / 1e12
+            r = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+        r["kernel"] = sorted({p["kernel"] for p in sel})
+        r["cases"] = [f"K={p['K']} N={p['N']} M={p['M']}" for p in sel]
+        r["per_launch_bytes_avg"] = round(sum(p["_tb"] for p in sel) / len(sel))
+        r["per_launch_flops_avg"] = round(sum(p["_flops"] for p in sel) / len(sel))
+        r["avg_launch_us"] = round(us / len(sel), 3)
+        out.append(r)
+    return out
+
+
+class Bench:
+    def __init__(self, args, torch, W):
+        self.args, self.torch, self.W = args, torch, W
+        self.stream = torch.cuda.current_stream()
+
+    # ---- timing -------------------------------------------------------------
+    def timed(self, fn, count, replays=1):
+        """Milliseconds for the launches that fn(count) enqueues, HIP events on
+        the launch stream.  By default fn's launches are recorded once into a
+        HIP graph, which is replayed once untimed (upload) and then ``replays``
+        times, each timed on its own; the median is returned."""
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if self.args.eager:
+            ts = []
+            for _ in range(replays):
+                torch.cuda.synchronize()
+                e0.record(self.stream)
+                fn(count)
+                e1.record(self.stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return statistics.median(ts)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(count)
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(replays):
+            e0.record(self.stream)
+            g.replay()
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        del g
+        return statistics.median(ts)
+
+    # ---- workloads ----------------------------------------------------------
+    def setup(self, name):
+        """Layers (repacked, weight copies for rotation) and per-case buffers."""
+        import dataclasses
+        torch, W = self.torch, self.W
+        from synthetic import CONFIGS, make_acts, make_layer_inputs
+        cases = [c for c in CONFIGS if c.cfg_id == CFG_ID[name]]
+        gs = self.args.group_size
+        if gs:
+            cases = [dataclasses.replace(c, group_size=gs, has_gidx=c.has_gidx and gs != -1) for c in cases]
+        layers, repack = [], []
+        for c in cases:
+            Lw = make_layer_inputs(c)
+            dev = {k: _to_dev(torch, v) for k, v in Lw.items()}
+            lyr = W.W4A16Linear(c.K, c.N, c.group_size, c.has_zeros, c.has_gidx, c.dtype, c.fmt)
+            lyr.process_weights_after_loading(dev["qweight"], dev["qzeros"], dev["scales"], dev["g_idx"])  # warm
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            lyr.process_weights_after_loading(dev["qweight"], dev["qzeros"], dev["scales"], dev["g_idx"])
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            rp_ms = e0.elapsed_time(e1)
+            repack.append({"shape": [c.K, c.N], "ms": round(rp_ms, 4),
+                           "packed_GBps": round((c.K * c.N / 2) / (rp_ms * 1e-3) / 1e9, 1)})
+            t = lyr.tiled
+            per_set = sum(v.numel() * v.element_size() for v in t.values() if v is not None)
+            R = max(2, math.ceil(ROTATE_BYTES / per_set))
+            sets = [t] + [{k: (v.clone() if v is not None else None) for k, v in t.items()} for _ in range(R - 1)]
+            del dev
+            layers.append((c, lyr, sets))
+        runs = []
+        for c, lyr, sets in layers:
+            for M in c.Ms:
+                xd = _to_dev(torch, make_acts(c, M))
+                yd = torch.empty((M, c.N), dtype=xd.dtype, device="cuda")
+                ws_b = W.w4_workspace_size(lyr.layer, M)
+                ws = torch.zeros((max(ws_b, 1),), dtype=torch.uint8, device="cuda")
+                runs.append(dict(c=c, M=M, lyr=lyr, sets=sets, x=xd, y=yd, ws=ws, ws_b=ws_b, i=0,
+                                 kernel=lyr.kernel_name(M)))
+        return cases, runs, repack
+
+    def launch(self, r):
+        # the current stream: the capture stream while a HIP graph is recorded
+        t = r["sets"][r["i"] % len(r["sets"])]
+        r["i"] += 1
+        self.W.w4a16_linear(r["lyr"].layer, r["M"], r["x"], t["qweight"], t["scales"], t["qzeros"], t["perm"], None,
+                            r["y"], r["ws"] if r["ws_b"] else None, r["ws_b"], self.torch.cuda.current_stream())
+
+    def per_case(self, runs):
+        """Each case alone: a graph of back-to-back launches (rotating weight
+        copies), the median of REPLAYS timed replays, per launch."""
+        torch = self.torch
+        out = []
+        for r in runs:
+            c, M = r["c"], r["M"]
+            for _ in range(3):
+                self.launch(r)
+            torch.cuda.synchronize()
+            if self.args.reps:
+                reps = self.args.reps
+            else:
+                est = self.timed(lambda n: [self.launch(r) for _ in range(n)], len(r["sets"]), 1) / len(r["sets"])
+                # ~20 ms of launches per replay, at least one pass over the copies, at most 400
+                reps = int(min(400, max(len(r["sets"]), 20.0 / max(est, 1e-4))))
+            us = self.timed(lambda n: [self.launch(r) for _ in range(n)], reps, REPLAYS) * 1e3 / reps
+            wb, tb = case_bytes(c, M)
+            flops = 2.0 * M * c.K * c.N
+            out.append(dict(K=c.K, N=c.N, M=M, kernel=r["kernel"], us=round(us, 3), reps=reps,
+                            weight_GBps=round(wb / (us * 1e-6) / 1e9, 1),
+                            total_GBps=round(tb / (us * 1e-6) / 1e9, 1),
+                            TFLOPS=round(flops / (us * 1e-6) / 1e12, 2),
+                            pct_hbm=round(100 * tb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+                            pct_mfma=round(100 * flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 1),
+                            _wb=wb, _tb=tb, _flops=flops, _us=us))
+        return out
+
+    def block(self, name, cases, runs, per_case, repack):
+        c0 = cases[0]
+        sum_us = sum(p["_us"] for p in per_case)
+        wb = sum(p["_wb"] for p in per_case)
+        fl = sum(p["_flops"] for p in per_case)
+        roof = roofline_of(per_case)
+        blk = {
+            "workload": f"{name}: " + ", ".join(f"(K={c.K},N={c.N})" for c in cases)
+                        + f" x M in {list(c0.Ms)}; {c0.fmt.upper()} "
+                        + ("per-channel" if c0.group_size == -1 else f"g={c0.group_size}")
+                        + (" zeros" if c0.has_zeros else " symmetric") + (" act-order" if c0.has_gidx else "")
+                        + ("" if len({c.group_size for c in cases}) == 1 else " (+ per-channel variant)"),
+            "act_dtype": c0.dtype,
+            "cases": len(per_case),
+            # each case once, back to back: packed-weight GB/s and flops of the set
+            "weight_GBps": round(wb / (sum_us * 1e-6) / 1e9, 1),
+            "TFLOPS": round(fl / (sum_us * 1e-6) / 1e12, 2),
+            "sum_case_us": round(sum_us, 3),
+            "roofline": roof,
+            "per_case": [{k: v for k, v in p.items() if not k.startswith("_")} for p in per_case],
+            "repack": repack,
+        }
+        return blk
+
+    def workload(self, name):
+        cases, runs, repack = self.setup(name)
+        pc = self.per_case(runs)
+        return cases, runs, pc, self.block(name, cases, runs, pc, repack)
+
+    def steps(self, runs):
+        """The timed steps of the headline: K passes over every case."""
+        torch, args = self.torch, self.args
+        for _ in range(args.warmup):
+            for r in runs:
+                self.launch(r)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ms = self.timed(lambda n: [self.launch(r) for _ in range(n) for r in runs], args.steps, 1) / args.steps
+        return ms, time.perf_counter() - t0
+
+
+def copy_probe(torch):
+    """A plain device copy of known size (not timed): the reference that the
+    HBM byte counters of a profiled run are scaled by."""
+    src = torch.empty((COPY_PROBE_BYTES,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def main():
@@ -107,161 +315,42 @@ def main():
 
     import torch
     import weight_only_int4_gptq_amd as W
-    from synthetic import CONFIGS, make_acts, make_layer_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     W.lib()
     if args.config == "moe":
         return main_moe(args, torch, W)
-    cfg_id = {"tiny": 1, "decode": 2, "mid": 3, "prefill": 4, "actorder": 5}[args.config]
-    cases = [c for c in CONFIGS if c.cfg_id == cfg_id]
-    if args.group_size:
-        import dataclasses
-        cases = [dataclasses.replace(c, group_size=args.group_size, has_gidx=c.has_gidx and args.group_size != -1)
-                 for c in cases]
-    stream = torch.cuda.current_stream()
+    B = Bench(args, torch, W)
+    head = "decode" if args.config == "all" else args.config
+    others = [w for w in WORKLOADS if w != head] if args.config == "all" else []
 
-    # ---- one-time repack (timed separately) and rotated weight copies ----
-    layers = []
-    repack = []
-    for c in cases:
-        Lw = make_layer_inputs(c)
-        dev = {k: _to_dev(torch, v) for k, v in Lw.items()}
-        lyr = W.W4A16Linear(c.K, c.N, c.group_size, c.has_zeros, c.has_gidx, c.dtype, c.fmt)
-        lyr.process_weights_after_loading(dev["qweight"], dev["qzeros"], dev["scales"], dev["g_idx"])  # warm
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        lyr.process_weights_after_loading(dev["qweight"], dev["qzeros"], dev["scales"], dev["g_idx"])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        rp_ms = e0.elapsed_time(e1)
-        repack.append({"shape": [c.K, c.N], "ms": round(rp_ms, 4),
-                       "packed_GBps": round((c.K * c.N / 2) / (rp_ms * 1e-3) / 1e9, 1)})
-        t = lyr.tiled
-        per_set = sum(v.numel() * v.element_size() for v in t.values() if v is not None)
-        R = max(2, math.ceil(ROTATE_BYTES / per_set))
-        sets = [t] + [{k: (v.clone() if v is not None else None) for k, v in t.items()} for _ in range(R - 1)]
-        del dev
-        layers.append((c, lyr, sets))
-    torch.cuda.synchronize()
-
-    # ---- activations / outputs per case ----
-    runs = []
-    for c, lyr, sets in layers:
-        for M in c.Ms:
-            x = make_acts(c, M)
-            xd = _to_dev(torch, x)
-            yd = torch.empty((M, c.N), dtype=xd.dtype, device="cuda")
-            ws_b = W.w4_workspace_size(lyr.layer, M)
-            ws = torch.zeros((max(ws_b, 1),), dtype=torch.uint8, device="cuda")
-            runs.append(dict(c=c, M=M, lyr=lyr, sets=sets, x=xd, y=yd, ws=ws, ws_b=ws_b, i=0,
-                             kernel=lyr.kernel_name(M)))
-
-    def launch(r):
-        # the current stream: the capture stream while a HIP graph is recorded
-        t = r["sets"][r["i"] % len(r["sets"])]
-        r["i"] += 1
-        W.w4a16_linear(r["lyr"].layer, r["M"], r["x"], t["qweight"], t["scales"], t["qzeros"], t["perm"], None,
-                       r["y"], r["ws"] if r["ws_b"] else None, r["ws_b"], torch.cuda.current_stream())
-
-    def step():
-        for r in runs:
-            launch(r)
-
-    def timed(fn, count):
-        """Milliseconds for the launches that fn() enqueues, HIP events on the
-        launch stream.  By default fn's launches are recorded once into a HIP
-        graph, which is replayed once untimed (upload) and once timed, so the
-        host's per-call cost (Python, ctypes, validation: ~5 us) does not
-        starve the GPU between short kernels, as in a serving loop."""
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        if args.eager:
-            torch.cuda.synchronize()
-            e0.record(stream)
-            fn(count)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn(count)
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        del g
-        return e0.elapsed_time(e1)
-
-    # ---- per-kernel timing: HIP events on the launch stream ----
-    per_case = []
-    for r in runs:
-        c, M = r["c"], r["M"]
-        reps = args.reps or max(len(r["sets"]), 40)
-        for _ in range(5):
-            launch(r)
-        torch.cuda.synchronize()
-        us = timed(lambda n: [launch(r) for _ in range(n)], reps) * 1e3 / reps
-        wb, tb = case_bytes(c, M)
-        flops = 2.0 * M * c.K * c.N
-        per_case.append(dict(K=c.K, N=c.N, M=M, kernel=r["kernel"], us=round(us, 3),
-                             weight_GBps=round(wb / (us * 1e-6) / 1e9, 1),
-                             total_GBps=round(tb / (us * 1e-6) / 1e9, 1),
-                             TFLOPS=round(flops / (us * 1e-6) / 1e12, 2),
-                             pct_hbm=round(100 * tb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
-                             pct_mfma=round(100 * flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 1),
-                             _wb=wb, _tb=tb, _flops=flops, _us=us))
-
-    # ---- copy of known size (not timed): the reference for the HBM byte
-    # counters when this run is profiled (FETCH_SIZE / WRITE_SIZE) ----
-    src = torch.empty((COPY_PROBE_BYTES,), dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    del src, dst
-
-    # ---- the timed steps ----
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ms_step = timed(lambda n: [step() for _ in range(n)], args.steps) / args.steps
-    wall = time.perf_counter() - t0
-
+    cases, runs, per_case, blk = B.workload(head)
+    copy_probe(torch)
+    ms_step, wall = B.steps(runs)
     wbytes_step = sum(case_bytes(r["c"], r["M"])[0] for r in runs)
     flops_step = sum(2.0 * r["M"] * r["c"].K * r["c"].N for r in runs)
     value = wbytes_step / (ms_step * 1e-3) / 1e9
+    unfused = {head: compare_unfused(torch, runs, per_case, B.stream)} if args.compare else None
 
-    # roofline of the GEMM kernel: algorithmic bytes (or flops) / launch time
-    sum_tb = sum(p["_tb"] for p in per_case)
-    sum_fl = sum(p["_flops"] for p in per_case)
-    sum_us = sum(p["_us"] for p in per_case)
-    hbm_bound = (sum_fl / (sum_tb)) < (MFMA_F16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
-    if hbm_bound:
-        ach = sum_tb / (sum_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
-    else:
-        ach = sum_fl / (sum_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
-    if hbm_bound and args.config == "decode":
+    # headline roofline: the head workload's dominant bound
+    roofs = blk["roofline"]
+    roof = dict(max(roofs, key=lambda r: r["avg_launch_us"] * len(r["cases"])))
+    if roof["bound"] == "hbm" and head == "decode" and not args.group_size:
         roof["traffic"] = measured_traffic()
-    roof["kernel"] = sorted({p["kernel"] for p in per_case})
-    roof["per_launch_bytes_avg"] = round(sum_tb / len(per_case))
-    roof["avg_launch_us"] = round(sum_us / len(per_case), 3)
+    del runs
+    torch.cuda.empty_cache()
 
-    unfused = compare_unfused(torch, runs, per_case, stream) if args.compare else None
+    blocks = {head: blk}
+    for w in others:
+        cw, rw, pw, bw = B.workload(w)
+        blocks[w] = bw
+        if args.compare:
+            unfused[w] = compare_unfused(torch, rw, pw, B.stream)
+        del rw
+        torch.cuda.empty_cache()
 
     cpu = None if args.no_cpu else cpu_baseline(cases, args.cpu_seconds)
-
-    for p in per_case:
-        for k in ("_wb", "_tb", "_flops", "_us"):
-            p.pop(k)
     c0 = cases[0]
     out = {
         "metric": METRIC,
@@ -277,21 +366,19 @@ def main():
         "dtype": "f16" if c0.dtype == "fp16" else "bf16",
         "data": "synthetic (seeded uniform int4 codes/zeros, uniform scales, N(0,1) activations)",
         "config": {
-            "workload": f"{args.config}: " + ", ".join(f"(K={c.K},N={c.N})" for c in cases)
-                        + f" x M in {list(c0.Ms)}; {c0.fmt.upper()} g={c0.group_size}"
-                        + (" zeros" if c0.has_zeros else " symmetric") + (" act-order" if c0.has_gidx else ""),
-            "cases": len(runs), "act_dtype": c0.dtype, "weight_rotation_MiB": ROTATE_BYTES >> 20,
+            "workload": blk["workload"],
+            "cases": len(per_case), "act_dtype": c0.dtype, "weight_rotation_MiB": ROTATE_BYTES >> 20,
             "copy_probe_MiB": COPY_PROBE_BYTES >> 20,
         },
         "timing": ("eager launches" if args.eager else
-                   "HIP graph of the timed launches (one untimed replay uploads it, one replay is timed)"),
+                   "HIP graph of the K timed steps (one untimed replay uploads it, one replay is timed); "
+                   f"per case: median of {REPLAYS} replays of a graph of back-to-back launches"),
         "tflops_step": round(flops_step / (ms_step * 1e-3) / 1e12, 3),
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
-        "dequant_then_gemm": unfused,
         "cpu_baseline": cpu,
-        "per_case": per_case,
-        "repack": repack,
+        "workloads": blocks,
+        "dequant_then_gemm": unfused,
     }
     print(json.dumps(out), flush=True)
 
@@ -306,7 +393,7 @@ MOE_E, MOE_K, MOE_N, MOE_TOKENS, MOE_TOPK = 8, 4096, 28672, (16, 256, 2048), 2
 
 def main_moe(args, torch, W):
     from synthetic import normal_acts, random_words, seeded, uniform_scales
-    stream = torch.cuda.current_stream()
+    B = Bench(args, torch, W)
     E, K, N = MOE_E, MOE_K, MOE_N
     G = K // 128
     experts = []
@@ -338,19 +425,6 @@ def main_moe(args, torch, W):
         W.w4a16_moe_linear(moe.layer, E, r["rows"], r["max_rows"], r["x"], r["offs"], t["qweight"], t["scales"],
                            t["qzeros"], None, r["y"], torch.cuda.current_stream())
 
-    def timed(fn, count):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn(count)
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)
-
     wbytes = E * K * N // 2
     per_case = []
     for r in runs:
@@ -358,50 +432,32 @@ def main_moe(args, torch, W):
             launch(r)
         torch.cuda.synchronize()
         reps = 20 if r["rows"] >= 1024 else 60
-        us = timed(lambda n: [launch(r) for _ in range(n)], reps) * 1e3 / reps
+        us = B.timed(lambda n: [launch(r) for _ in range(n)], reps, REPLAYS) * 1e3 / reps
         tb = wbytes + E * G * N * 2 + E * G * N // 2 + r["rows"] * (K + N) * 2
         fl = 2.0 * r["rows"] * K * N
-        per_case.append(dict(tokens=r["T"], rows=r["rows"], rows_per_expert=r["counts"], us=round(us, 3),
-                             weight_GBps=round(wbytes / (us * 1e-6) / 1e9, 1), TFLOPS=round(fl / (us * 1e-6) / 1e12, 2),
-                             _tb=tb, _fl=fl, _us=us))
-
-    def step():
-        for r in runs:
-            launch(r)
+        per_case.append(dict(K=K, N=N, M=r["rows"], tokens=r["T"], rows_per_expert=r["counts"],
+                             kernel="w4a16_moe_linear", us=round(us, 3),
+                             weight_GBps=round(wbytes / (us * 1e-6) / 1e9, 1),
+                             TFLOPS=round(fl / (us * 1e-6) / 1e12, 2), _tb=tb, _flops=fl, _us=us))
 
     for _ in range(args.warmup):
-        step()
+        for r in runs:
+            launch(r)
     torch.cuda.synchronize()
     t0w = time.perf_counter()
-    ms_step = timed(lambda n: [step() for _ in range(n)], args.steps) / args.steps
+    ms_step = B.timed(lambda n: [launch(r) for _ in range(n) for r in runs], args.steps, 1) / args.steps
     wall = time.perf_counter() - t0w
     value = len(runs) * wbytes / (ms_step * 1e-3) / 1e9
-    sum_tb = sum(p["_tb"] for p in per_case)
-    sum_fl = sum(p["_fl"] for p in per_case)
-    sum_us = sum(p["_us"] for p in per_case)
-    if sum_fl / sum_tb < (MFMA_F16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9):
-        ach = sum_tb / (sum_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
-    else:
-        ach = sum_fl / (sum_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
-    roof["kernel"] = ["w4a16_moe_linear (wide kernel, grouped)"]
-    roof["avg_launch_us"] = round(sum_us / len(per_case), 3)
+    roofs = roofline_of(per_case)
     cpu = None
     if not args.no_cpu:
         import oracle as O
-        qw, qz, sc = experts[0]
         xs = normal_acts(seeded(9, 4, K), (4, K), "fp16")
         tc = time.perf_counter()
         O.reference_moe(xs, np.array([0, 4]), "awq", "fp16", [experts[0]], 128)
         dt = time.perf_counter() - tc
-        cpu = {"value": round((K * N // 2) / dt / 1e9, 4), "unit": "GB/s", "cores": os.cpu_count(), "kind": "oracle",
-               "sample": "one expert (K=4096, N=28672) on 4 rows", "seconds": round(dt, 2)}
-    for p in per_case:
-        for k in ("_tb", "_fl", "_us"):
-            p.pop(k)
+        cpu = {"value": round((K * N // 2) / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads(),
+               "kind": "oracle", "sample": "one expert (K=4096, N=28672) on 4 rows", "seconds": round(dt, 2)}
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
@@ -410,8 +466,9 @@ def main_moe(args, torch, W):
         "config": {"workload": f"moe: E={E} experts of (K={K},N={N}) AWQ g=128 zeros, top-{MOE_TOPK} routing of "
                                f"{list(MOE_TOKENS)} tokens", "cases": len(runs), "act_dtype": "fp16",
                    "weight_rotation_MiB": ROTATE_BYTES >> 20},
-        "timing": "HIP graph of the timed launches (one untimed replay uploads it, one replay is timed)",
-        "wall_s_timed": round(wall, 3), "roofline": roof, "cpu_baseline": cpu, "per_case": per_case,
+        "timing": f"HIP graph of the timed launches; per case: median of {REPLAYS} replays",
+        "wall_s_timed": round(wall, 3), "roofline": roofs[-1], "roofline_all": roofs, "cpu_baseline": cpu,
+        "per_case": [{k: v for k, v in p.items() if not k.startswith("_")} for p in per_case],
     }
     print(json.dumps(out), flush=True)
 
@@ -421,7 +478,7 @@ def compare_unfused(torch, runs, per_case, stream):
     dense dequantization kernel writes W [K, N] in the activation dtype, then
     torch.matmul (the vendor GEMM) computes x W.  Each part is timed with HIP
     events over back-to-back direct launches, per case, next to the fused
-    kernel's time from the roofline timing."""
+    kernel's time from the per-case timing."""
     out = []
     for r, pc in zip(runs, per_case):
         lyr, M = r["lyr"], r["M"]
@@ -456,39 +513,75 @@ def compare_unfused(torch, runs, per_case, stream):
     return out
 
 
-def cpu_baseline(cases, seconds):
-    """The CPU oracle, as it stands, on a bounded sample of the workload:
-    whole-layer reference (unpack, order fix, float64 dequant, float64 matmul)
-    for the workload's cases in order until ``seconds`` of CPU time are spent.
-    Value in the metric's unit (packed-weight GB/s)."""
-    import oracle as O
-    from synthetic import make_acts, make_layer_inputs
+def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
-    done, wbytes, spent = [], 0, 0.0
+        return os.cpu_count() or 1
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(cases, seconds):
+    """The CPU oracle, as it stands, on a bounded sample of the headline
+    workload: for each (layer, M) case in order, until ``seconds`` of CPU time
+    are spent, the oracle's three phases are timed separately:
+      1. unpack + AWQ order fix + standard repack (awq_to_std, then the
+         standard unpack to codes; NumPy integer ops, one thread),
+      2. float64 dequantization per group (one thread),
+      3. float64 matmul (BLAS dgemm on the BLAS threads).
+    ``value`` is packed-weight GB/s over the three phases together, in the
+    metric's unit."""
+    import oracle as O
+    from synthetic import make_acts, make_layer_inputs
+    ph = {"unpack_repack_s": 0.0, "dequant_s": 0.0, "matmul_s": 0.0}
+    done, wbytes = [], 0
+    spent = 0.0
     for _ in range(8):  # passes over the workload until `seconds` of CPU time are spent
         for c in cases:
             Lw = make_layer_inputs(c)
             for M in c.Ms:
                 x = make_acts(c, M)
                 t0 = time.perf_counter()
-                O.reference_linear(x, c.fmt, c.dtype, Lw["qweight"], Lw["qzeros"], Lw["scales"], c.group_size,
-                                   g_idx=Lw["g_idx"])
-                dt = time.perf_counter() - t0
-                spent += dt
+                if c.fmt == "awq":
+                    sw, sz = O.awq_to_std(Lw["qweight"], Lw["qzeros"])
+                else:
+                    sw, sz = Lw["qweight"], Lw["qzeros"]
+                q = O.unpack_std(sw)
+                z = None if sz is None else O.unpack_std_zeros(sz)
+                t1 = time.perf_counter()
+                Wd = O.dequant(q, z, O.act_to_f64(Lw["scales"], c.dtype),
+                               O.group_index(c.K, c.group_size, Lw["g_idx"]))
+                t2 = time.perf_counter()
+                O.linear_ref(O.act_to_f64(x, c.dtype), Wd)
+                t3 = time.perf_counter()
+                ph["unpack_repack_s"] += t1 - t0
+                ph["dequant_s"] += t2 - t1
+                ph["matmul_s"] += t3 - t2
+                spent += t3 - t0
                 wbytes += c.K * c.N // 2
                 done.append(f"(K={c.K},N={c.N},M={M})")
+                del Wd, q
                 if spent >= seconds:
                     break
             if spent >= seconds:
                 break
         if spent >= seconds:
             break
-    return {"value": round(wbytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(done)} whole-layer oracle calls cycling through the cases "
+    return {"value": round(wbytes / spent / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
+            "phases": {k: round(v, 3) for k, v in ph.items()},
+            "phase_threads": {"unpack_repack": 1, "dequant": 1, "matmul": blas_threads()},
+            "sample": f"{len(done)} oracle layer calls cycling through the decode cases "
                       + " ".join(dict.fromkeys(done)), "seconds": round(spent, 2)}
 
 

@@ -192,9 +192,11 @@ w4_status w4a16_linear(const w4_layer* layer, int64_t M, const void* x, const in
  *                  from 0 to total_rows.  Entries are clamped into
  *                  [0, total_rows] (bad offsets give wrong rows, never an
  *                  access outside x or y).
- *   max_rows       host upper bound on the rows of any one expert (sizes the
- *                  launch; rows of an expert beyond it are not computed), or
- *                  0 for total_rows
+ *   max_rows       host estimate of the rows of the largest expert, or 0 for
+ *                  total_rows.  It sizes the launch only: every row of every
+ *                  expert is computed whatever its value (workgroups walk
+ *                  further row tiles when an expert has more rows), so a
+ *                  low estimate costs time, never rows.
  *   tiled_qweight, tiled_scales, tiled_qzeros
  *                  the num_experts per-expert buffers of w4_repack_gptq,
  *                  each exactly w4_sizes() bytes, stacked in expert order

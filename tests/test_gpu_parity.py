@@ -5,9 +5,12 @@
 * GEMM outputs must satisfy the acceptance bound of the layer:
   max |y - ref| <= 1e-2 (1 + |ref|) elementwise and
   ||y - ref||_F / ||ref||_F <= 2e-3, against the float64 reference.
-  Small shapes are compared element by element; the full workload shapes, in
-  the launch configuration the benchmark times, on sampled outputs that the
-  oracle computes one by one.
+  Every comparison is element by element.  The workload shapes run at full
+  size in the launch configuration the benchmark times; their outputs are
+  compared in full, except for the largest prefill products, where every row
+  of a 1024-column window and every column of a 128-row window are compared
+  (and the (28672, 8192) layer at M = 2048 in full).  From 1e5 compared
+  outputs on, the bounds apply exactly as stated.
 """
 import os
 
@@ -206,13 +209,18 @@ def _rounding_floor(ref, dtype):
     return O.check(rr, ref)["rel_fro"]
 
 
+STRICT_MIN_OUTPUTS = 100_000
+
+
 def _assert_close(y_bits, ref, dtype, what):
-    """Acceptance bound of the layer.  The Frobenius bound is never made
-    stricter than the error of the correctly rounded reference: on a few
-    hundred bf16 outputs that rounding alone can exceed 2e-3."""
+    """Acceptance bound of the layer.  On fewer than STRICT_MIN_OUTPUTS
+    outputs the Frobenius bound is never made stricter than the error of the
+    correctly rounded reference (on a few hundred bf16 outputs that rounding
+    alone can exceed 2e-3); from STRICT_MIN_OUTPUTS on, the bound is 2e-3 as
+    stated."""
     y = O.act_to_f64(y_bits, dtype)
     floor = _rounding_floor(ref, dtype)
-    fro = max(FRO_TOL, 1.05 * floor)
+    fro = FRO_TOL if ref.size >= STRICT_MIN_OUTPUTS else max(FRO_TOL, 1.05 * floor)
     r = O.check(y, ref, ELEM_TOL, fro)
     say(f"  {what}: max_ratio={r['max_ratio']:.3e} rel_fro={r['rel_fro']:.3e} (rounding floor {floor:.3e})")
     assert r["ok"], (what, r, floor)
@@ -353,14 +361,24 @@ def test_loaded_library_is_in_tree(W):
 
 
 # ----------------------------------------------------------------------------
-# GEMM: every workload shape at full size, sampled outputs
+# GEMM: every workload shape at full size, element by element
 # ----------------------------------------------------------------------------
 
 _FULL = [(c, M) for c in CONFIGS for M in c.Ms]
 _cache = {}
+# Outputs are compared in full when the float64 product costs at most this
+# many flops on the host; above it (the prefill shapes) every row of a
+# 1024-column window and every column of a 128-row window are compared, and
+# the (28672, 8192) layer at M = 2048 is compared in full as well.
+FULL_COMPARE_FLOPS = 1.5e11
+FULL_COMPARE_ALWAYS = {("prefill", 28672, 8192, 2048)}
+ROW_CHUNK = 512
 
 
 def _full_layer(W, c):
+    """(inputs, layer, dequantized float64 weight [K, N]) of a workload shape;
+    the weight comes from the oracle's own unpack, order fix and
+    dequantization, once per shape."""
     if c.label not in _cache:
         _cache.clear()
         import torch
@@ -368,26 +386,72 @@ def _full_layer(W, c):
         Lw = make_layer_inputs(c)
         Lyr = _prepare(W, c.fmt, c.K, c.N, c.group_size, c.has_zeros, c.has_gidx, c.dtype, Lw["qweight"],
                        Lw["qzeros"], Lw["scales"], Lw["g_idx"])
-        _cache[c.label] = (Lw, Lyr)
+        _cache[c.label] = (Lw, Lyr, _dequant_weight(c, Lw))
     return _cache[c.label]
 
 
+def _dequant_weight(c, Lw):
+    """Oracle float64 weight [K, N]: unpack, order fix, per-group
+    dequantization.  Standard-format layers go through the oracle in
+    4096-column slices (the same functions on a narrower layer; the slices
+    keep the host's temporaries small), AWQ layers in one piece."""
+    grp = O.group_index(c.K, c.group_size, Lw["g_idx"])
+    if c.fmt == "awq":
+        q, z = O.codes_from_inputs(c.fmt, Lw["qweight"], Lw["qzeros"])
+        return O.dequant(q, z, O.act_to_f64(Lw["scales"], c.dtype), grp)
+    Wd = np.empty((c.K, c.N), dtype=np.float64)
+    for a in range(0, c.N, 4096):
+        b = min(a + 4096, c.N)
+        qz = None if Lw["qzeros"] is None else np.ascontiguousarray(Lw["qzeros"][:, a // 8:b // 8])
+        q, z = O.codes_from_inputs(c.fmt, np.ascontiguousarray(Lw["qweight"][:, a:b]), qz)
+        Wd[:, a:b] = O.dequant(q, z, O.act_to_f64(np.ascontiguousarray(Lw["scales"][:, a:b]), c.dtype), grp)
+    return Wd
+
+
+def _ref_rows(xs, Wd, r0, r1):
+    """float64 reference of rows [r0, r1), in chunks of ROW_CHUNK rows."""
+    out = np.empty((r1 - r0, Wd.shape[1]), dtype=np.float64)
+    for a in range(r0, r1, ROW_CHUNK):
+        b = min(a + ROW_CHUNK, r1)
+        out[a - r0:b - r0] = O.linear_ref(xs[a:b], Wd)
+    return out
+
+
+def _assert_strict(y_bits, ref, dtype, what):
+    """The acceptance bound as stated, for comparisons of >= 1e5 outputs."""
+    y = O.act_to_f64(y_bits, dtype)
+    r = O.check(y, ref, ELEM_TOL, FRO_TOL)
+    say(f"  {what}: {ref.size} outputs max_ratio={r['max_ratio']:.3e} rel_fro={r['rel_fro']:.3e}")
+    assert r["ok"], (what, r)
+    return r
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("c,M", _FULL, ids=[f"{c.label}-M{M}" for c, M in _FULL])
-def test_linear_full_size_sampled(W, c, M):
+def test_linear_full_size(W, c, M):
     say(f"full {c.label} M={M}")
-    Lw, Lyr = _full_layer(W, c)
+    Lw, Lyr, Wd = _full_layer(W, c)
     say(f"  kernel={Lyr.kernel_name(M)}")
     x = make_acts(c, M)
-    y, _ = _run_linear(W, Lyr, x, guard_rows=1)
-    yv = O.act_to_f64(y, c.dtype)
-    assert np.isfinite(yv).all()
+    y, guard = _run_linear(W, Lyr, x, guard_rows=1)
+    assert (guard.view(np.uint16) == 0x7F7F).all(), "write past row M"
+    xs = O.act_to_f64(x, c.dtype)
+    flops = 2.0 * M * c.K * c.N
+    if flops <= FULL_COMPARE_FLOPS or (c.name, c.K, c.N, M) in FULL_COMPARE_ALWAYS:
+        ref = _ref_rows(xs, Wd, 0, M)
+        _assert_strict(y, ref, c.dtype, f"{c.label} M={M} complete")
+        return
     rng = seeded(404, c.cfg_id, M, c.K, c.N)
-    ns = 1024
-    rows = np.concatenate([[0, M - 1], rng.integers(0, M, size=ns - 2)])
-    cols = np.concatenate([[0, c.N - 1], rng.integers(0, c.N, size=ns - 2)])
-    ref = O.reference_entries(x, c.fmt, c.dtype, Lw["qweight"], Lw["qzeros"], Lw["scales"], c.group_size, rows,
-                              cols, g_idx=Lw["g_idx"])
-    _assert_close(y[rows, cols], ref, c.dtype, f"{c.label} M={M} (sampled {ns})")
+    # every row, 1024 consecutive columns (a seeded window, 16-aligned)
+    c0 = int(rng.integers(0, (c.N - 1024) // 16 + 1)) * 16
+    ref = O.linear_ref(xs, Wd[:, c0:c0 + 1024])
+    _assert_strict(y[:, c0:c0 + 1024], ref, c.dtype, f"{c.label} M={M} rows 0..{M} x cols {c0}..{c0 + 1024}")
+    # every column, 128 consecutive rows (a seeded window), and the last row
+    r0 = int(rng.integers(0, M - 128 + 1))
+    ref = _ref_rows(xs, Wd, r0, r0 + 128)
+    _assert_strict(y[r0:r0 + 128], ref, c.dtype, f"{c.label} M={M} rows {r0}..{r0 + 128} x all cols")
+    ref = _ref_rows(xs, Wd, M - 1, M)
+    _assert_close(y[M - 1:M], ref, c.dtype, f"{c.label} M={M} last row")
 
 
 # ----------------------------------------------------------------------------
@@ -433,12 +497,8 @@ def test_linear_wide_tiles_sampled(W, v):
         bias = uniform_scales(seeded(508, N), (N,), -1.0, 1.0, dtype) if name.startswith("awq") else None
         y, guard = _run_linear(W, Lyr, x, bias, guard_rows=4)
         assert (guard.view(np.uint16) == 0x7F7F).all(), "write past row M"
-        ns = 2048
-        srng = seeded(507, M, N, len(name))
-        rows = np.concatenate([[0, M - 1, M - 1], srng.integers(0, M, size=ns - 3)])
-        cols = np.concatenate([[0, N - 1, 0], srng.integers(0, N, size=ns - 3)])
-        ref = O.reference_entries(x, fmt, dtype, qweight, qzeros, scales, gs, rows, cols, g_idx=g_idx, bias=bias)
-        _assert_close(y[rows, cols], ref, dtype, f"{name} M={M} N={N} (sampled {ns})")
+        ref = O.reference_linear(x, fmt, dtype, qweight, qzeros, scales, gs, g_idx=g_idx, bias=bias)
+        _assert_close(y, ref, dtype, f"{name} M={M} N={N} (all {M * N} outputs)")
 
 
 # ----------------------------------------------------------------------------
@@ -596,7 +656,9 @@ def test_moe_linear_matches_the_oracle(W, v):
             x = normal_acts(seeded(708, R, K, N), (R, K), dtype)
             bias = uniform_scales(seeded(709, E, N), (E, N), -1.0, 1.0, dtype) if with_bias else None
             ref = O.reference_moe(x, offsets, fmt, dtype, experts, gs, bias=bias)
-            for max_rows in (0, max(rows)):
+            # max_rows sizes the launch only: estimates below the largest
+            # expert (1, 17) must still compute every row
+            for max_rows in (0, max(rows), 1, 17):
                 say(f"moe {name} N={N} rows={rows} max_rows={max_rows}")
                 buf = filled((R + 2, N), act_dtype(dtype), 0x7F)
                 moe.apply(to_dev(x), to_dev(offsets), max_rows, to_dev(bias) if bias is not None else None,

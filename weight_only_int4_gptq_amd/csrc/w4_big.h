@@ -1,0 +1,299 @@
+// Large-M fused dequantize + GEMM on v_mfma_f32_32x32x16_f16 (gfx950).
+//
+// y[m, n] = sum_k x[m, k] * (q[k, n] - z[g(k), n]) * s[g(k), n] + bias[n]
+// (dequantization of the vLLM AWQ practice page, section 5.3, fused into the
+// matrix multiply as the learning-book page, section 5.3, describes; that
+// page's section 1 names large batches compute-bound).
+//
+// Why 32x32x16.  A 32x32x16 MFMA does twice the work of a 16x16x32 one per
+// operand register, so per flop it needs half the activation bytes from LDS
+// and half the weight dequantization.  With 16x16x32 tiles and the
+// activations read from LDS, a wave reads 0.5 KiB of LDS per 16-cycle MFMA
+// even with two strips per wave, which alone fills the CU's LDS read
+// bandwidth at the MFMA peak; a 128 x 64 wave tile of 32x32x16 MFMAs reads
+// 4 KiB per eight 32-cycle MFMAs, a quarter of it.
+//
+// Operand layout of v_mfma_f32_32x32x16_f16: lane l supplies row (A) or
+// column (B) l % 32 and the eight K values 8 (l / 32) .. 8 (l / 32) + 7 of
+// the 16-deep step; output element r of lane l is row
+// 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+//
+// The weights stay in the library's tile layout (16-column strips, words
+// [t][b][l'][j] holding column 16 t + l' % 16 at rows
+// 128 b + 32 j + 8 (l' / 16) + e).  Lane l of a 32-column tile (strips 2 T
+// and 2 T + 1) needs column c = l % 32 at rows 16 s + 8 h + e (h = l / 32)
+// for the eight 16-deep steps s of a block: for even s that is word j = s / 2
+// of lane l' = 16 h + c % 16 of strip 2 T + c / 16, for odd s word j = s / 2
+// of lane l' + 32.  So each lane loads two 16-byte chunks per tile and block,
+// and a step's B operand is one word, dequantized to eight exact (q - z)
+// halves exactly as in the 16x16x32 kernels.
+//
+// Numerics: exact integer operands, fp32 accumulation, one fp32 scale per
+// period applied with the ratio rescale of the wide kernel (the accumulator
+// holding sum_{h<g} P_h s_h / s_{g-1} is multiplied by s_{g-1} / s_g at the
+// start of period g and by the last scale at the end; the tile layout never
+// stores a zero scale), y rounded once.
+//
+// Workgroup: WM x WN waves, each owning MT 32-row tiles and NT 32-column
+// tiles (workgroup tile 32 MT WM x 32 NT WN).  K is walked in 128-row blocks
+// through an S-deep pipeline: the activation tile of block b sits in LDS slot
+// b % S (direct global->LDS loads, 16-byte chunk j of row r stored at chunk
+// position j ^ (r % 16), so the rows one A read touches fall on distinct
+// banks), the packed words, scales and zeros of block b in register slot
+// b % S.  Iteration b waits until its own block has landed (vmcnt counted as
+// in the wide kernel), passes one barrier, issues block b + S - 1 and
+// computes block b.
+//
+// Workgroup -> tile: the dispatcher hands consecutive workgroups to the
+// eight XCDs in turn; the grid is remapped so that each XCD walks a
+// contiguous range of tiles, in bands of group_m row tiles, so tiles that
+// share activation rows or weight columns run on the same L2.
+#pragma once
+
+#include "w4_kern.h"
+
+namespace w4 {
+namespace {
+
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f16v mfma32(u4 a, u4 b, f16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(bit_as<h8>(a), bit_as<h8>(b), c, 0, 0, 0);
+}
+
+template <int WM, int WN, int MT, int NT, int S>
+struct BigCfg {
+  static constexpr int NW = WM * WN;
+  static constexpr int BM = 32 * MT * WM;                    // rows per workgroup tile
+  static constexpr int BN = 32 * NT * WN;                    // columns per workgroup tile
+  static constexpr int NA = BM * kTileK * 2 / (1024 * NW);   // 1 KiB direct-to-LDS loads per wave per block
+  static constexpr int kAfter = (S - 2) * (2 * NT + NA);     // loads of the S - 2 later blocks
+  static_assert(NA >= 1 && NA * 1024 * NW == BM * kTileK * 2, "the activation tile splits evenly over the waves");
+  static_assert(S >= 2 && S <= 4 && kAfter < 64, "pipeline depth");
+};
+
+// Workgroup id -> (row tile, column tile), see the header comment.
+__device__ __forceinline__ void big_tile_of(int64_t L, int64_t tiles_m, int64_t tiles_n, int64_t group_m,
+                                            int64_t& tm, int64_t& tn) {
+  const int64_t ntiles = tiles_m * tiles_n;
+  if (ntiles % 8 == 0) L = (L % 8) * (ntiles / 8) + L / 8;
+  const int64_t per_band = group_m * tiles_n;
+  const int64_t band = L / per_band, first = band * group_m;
+  const int64_t rows = tiles_m - first < group_m ? tiles_m - first : group_m;
+  const int64_t in = L - band * per_band;
+  tm = first + in % rows;
+  tn = in / rows;
+}
+
+template <int WM, int WN, int MT, int NT, int S, int GM, bool HAS_Z>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __restrict__ x,
+                                                             const u4* __restrict__ qw,
+                                                             const uint16_t* __restrict__ sc,
+                                                             const uint32_t* __restrict__ zs,
+                                                             const uint16_t* __restrict__ bias,
+                                                             uint16_t* __restrict__ y, float* __restrict__ part,
+                                                             int64_t M, int64_t K, int64_t N, int G,
+                                                             int64_t tiles_m, int64_t tiles_n, int64_t group_m) {
+  using C = BigCfg<WM, WN, MT, NT, S>;
+  constexpr int NP = Groups<GM>::kPeriods;  // scale periods per 128-row block
+  constexpr int SPP = 8 / NP;               // 16-deep steps per period
+  constexpr int NA = C::NA;
+  constexpr int kSlot = C::BM * kTileK, kNone = 8;
+  // one LDS array per pipeline slot (see the wide kernel)
+  __shared__ __attribute__((aligned(1024))) uint16_t lds0[kSlot];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds1[kSlot];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds2[S > 2 ? kSlot : kNone];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds3[S > 3 ? kSlot : kNone];
+  auto slot_lds = [&](int u) __attribute__((always_inline)) -> uint16_t* {
+    switch (u) {
+      case 0: return lds0;
+      case 1: return lds1;
+      case 2: return lds2;
+      default: return lds3;
+    }
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int c = lane & 31, h = lane >> 5;
+  const int64_t T = (N + kTileN - 1) / kTileN;  // strips; the last may be half padding
+  const int64_t nblk = K / kTileK;
+  const int64_t split = blockIdx.y, nsplit = gridDim.y;  // split-K ranges of blocks
+  const int64_t kb0 = nblk * split / nsplit;
+  const int64_t nb = nblk * (split + 1) / nsplit - kb0;
+  int64_t tm, tn;
+  big_tile_of(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+  const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
+  const uint32_t zshift = 4u * (uint32_t)(c & 7);
+  const NibbleMasks nm = NibbleMasks::make();
+
+  // weights, scales, zeros of the lane's column in each 32-column tile
+  // (strips past the end read strip 0 and are never stored)
+  const u4* wp[NT];
+  const uint16_t* sp[NT];
+  const uint32_t* zp[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int64_t t = (n0 + (int64_t)(wn * NT + nt) * 32) / kTileN + (c >> 4);
+    const int64_t tt = t < T ? t : 0;
+    wp[nt] = qw + tt * nblk * 64 + (c & 15) + 16 * h;
+    sp[nt] = sc + tt * G * kTileN + (c & 15);
+    zp[nt] = HAS_Z ? zs + tt * G * 2 + ((c & 15) >> 3) : nullptr;
+  }
+  // staging: load i of this wave fills rows 4 (NA wave + i) .. + 3 of the
+  // tile; lane l lands at chunk position l % 16 of row base + l / 16 and so
+  // loads logical chunk (l % 16) ^ (row % 16)
+  const uint16_t* ap[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int row = 4 * (NA * wave + i) + (lane >> 4);
+    int64_t m = m0 + row;
+    m = m < M ? m : M - 1;
+    ap[i] = x + m * K + 8 * ((lane & 15) ^ (row & 15));
+  }
+
+  struct Slot {
+    u4 w[NT][2];
+    uint16_t s[NT][NP];
+    uint32_t z[NT][NP];
+  };
+  Slot rg[S];
+
+  auto issue = [&](int64_t b, Slot& r, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int64_t g = Groups<GM>::group((int)b, p);
+        r.s[nt][p] = sp[nt][g * kTileN];
+        r.z[nt][p] = HAS_Z ? zp[nt][g * 2] : 0u;
+      }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      r.w[nt][0] = wp[nt][b * 64];
+      r.w[nt][1] = wp[nt][b * 64 + 32];
+    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) load_lds16(ap[i] + b * kTileK, slot_lds(slot) + 4 * (NA * wave + i) * kTileK);
+  };
+
+  f16v acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][nt][r] = 0.f;
+  float s_prev[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) s_prev[nt] = 1.f;
+
+  auto compute = [&](const Slot& r, int slot) __attribute__((always_inline)) {
+    // row of this lane in row tile i: 32 (MT wm + i) + c, so row % 16 == c % 16
+    const uint16_t* xa = slot_lds(slot) + (wm * MT * 32 + c) * kTileK;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      uint32_t n1[NT], n2[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint32_t z = HAS_Z ? (r.z[nt][p] >> zshift) & 0xFu : 8u;
+        n1[nt] = nz1024_bits(z);
+        n2[nt] = nz64_bits(z);
+        const float s_cur = act_to_f32<false>(r.s[nt][p]);
+        if constexpr (GM != GM_CH) {
+          const float ratio = s_prev[nt] * __builtin_amdgcn_rcpf(s_cur);
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][nt][q] *= ratio;
+        }
+        s_prev[nt] = s_cur;
+      }
+#pragma unroll
+      for (int st = 0; st < SPP; ++st) {
+        const int step = p * SPP + st;  // 16-deep step of the block, 0..7
+        u4 a[MT];
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          a[i] = *reinterpret_cast<const u4*>(xa + i * 32 * kTileK + 8 * ((2 * step + h) ^ (c & 15)));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint32_t w = r.w[nt][step & 1][step >> 1];
+          const u4 bq = dq_f16(w, n1[nt], n2[nt], nm);
+#pragma unroll
+          for (int i = 0; i < MT; ++i) acc[i][nt] = mfma32(a[i], bq, acc[i][nt]);
+        }
+      }
+    }
+  };
+
+  auto iterate = [&](int64_t b, int u) __attribute__((always_inline)) {
+    const int un = (u + S - 1) % S;
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<C::kAfter>();
+    lds_barrier();
+    const int64_t bn = b + S - 1 < nb ? b + S - 1 : nb - 1;  // clamped: a redundant in-bounds load
+    issue(kb0 + bn, rg[un], un);
+    compute(rg[u], u);
+  };
+
+#pragma unroll
+  for (int u = 0; u < S - 1; ++u) issue(kb0 + (u < nb ? u : nb - 1), rg[u], u);
+  int64_t b = 0;
+  for (; b + S <= nb; b += S) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) iterate(b + u, u);
+  }
+#pragma unroll
+  for (int u = 0; u < S - 1; ++u)
+    if (b + u < nb) iterate(b + u, u);
+
+  // epilogue: element r of lane l is row 8 (r / 4) + 4 h + r % 4 of each row
+  // tile, column c of each column tile
+  float* pz = part != nullptr ? part + split * M * N : nullptr;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int64_t n = n0 + (int64_t)(wn * NT + nt) * 32 + c;
+    if (n >= N) continue;  // padded columns, or tiles past the last strip
+    const float bv = bias != nullptr && pz == nullptr ? act_to_f32<false>(bias[n]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + (int64_t)(wm * MT + i) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m >= M) continue;
+        const float v = acc[i][nt][r] * s_prev[nt];
+        if (pz != nullptr)
+          pz[m * N + n] = v;
+        else
+          y[m * N + n] = f32_to_act<false>(v + bv);
+      }
+  }
+}
+
+// Launch of one configuration (fp16 only); `group_m` row tiles per band of
+// the tile order.
+template <int WM, int WN, int MT, int NT, int S, int GM, bool HZ>
+hipError_t run_big(const Args& a, const uint16_t* x, int64_t group_m, hipStream_t st) {
+  using C = BigCfg<WM, WN, MT, NT, S>;
+  const int64_t Np = (a.N + kTileN - 1) / kTileN * kTileN;
+  const int64_t tiles_m = (a.M + C::BM - 1) / C::BM, tiles_n = (Np + C::BN - 1) / C::BN;
+  const int splits = a.splits > 1 ? a.splits : 1;
+  if (splits > 1 && (a.part == nullptr || splits > a.K / kTileK)) return hipErrorInvalidValue;
+  if (tiles_m * tiles_n > 0x7FFFFFFF || group_m < 1) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits);
+  gemm_big<WM, WN, MT, NT, S, GM, HZ><<<grid, 64 * WM * WN, 0, st>>>(
+      x, a.qw, a.sc, a.zs, a.bias, a.y, splits > 1 ? a.part : nullptr, a.M, a.K, a.N, a.G, tiles_m, tiles_n,
+      group_m);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t total4 = a.M * a.N / 4;
+  int64_t blocks = (total4 + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  split_reduce<false><<<(unsigned)blocks, 256, 0, st>>>(a.part, a.bias, a.y, a.M, a.N, splits);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace w4

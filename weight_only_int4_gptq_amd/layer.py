@@ -64,14 +64,14 @@ class W4A16Linear:
             std_w = torch.empty((K // 8, N), dtype=i32, device=d)
             std_z = torch.empty((G, N // 8), dtype=i32, device=d)
             A.w4_repack_awq(self.layer, qweight, qzeros, std_w, std_z, stream)
-        T = (N + 15) // 16  # strips; a last half strip is padded
-        Kp = (K + 127) // 128 * 128  # rows padded to whole 128-row blocks
-        Gp = 1 if self.group_size == -1 else Kp // self.group_size
+        # the tile layout's byte sizes come from the library (w4_sizes), the
+        # one place that knows its padding
+        sz = self.sizes
         tiled = {
-            "qweight": torch.empty((Kp * T * 2,), dtype=i32, device=d),
-            "scales": torch.empty((T, Gp, 16), dtype=_TORCH_DTYPE[self.dtype], device=d),
-            "qzeros": torch.empty((T, Gp, 2), dtype=i32, device=d) if self.has_zero_points else None,
-            "perm": torch.empty((K,), dtype=i32, device=d) if self.has_g_idx else None,
+            "qweight": torch.empty((sz["tiled_qweight"] // 4,), dtype=i32, device=d),
+            "scales": torch.empty((sz["tiled_scales"] // 2,), dtype=_TORCH_DTYPE[self.dtype], device=d),
+            "qzeros": torch.empty((sz["tiled_qzeros"] // 4,), dtype=i32, device=d) if self.has_zero_points else None,
+            "perm": torch.empty((sz["perm"] // 4,), dtype=i32, device=d) if self.has_g_idx else None,
         }
         status = torch.empty((1,), dtype=i32, device=d) if self.has_g_idx else None
         A.w4_repack_gptq(self.layer, std_w, std_z, scales, g_idx, tiled["qweight"], tiled["scales"],
@@ -88,28 +88,53 @@ class W4A16Linear:
 
     # -- apply -------------------------------------------------------------
     def apply(self, x: torch.Tensor, bias=None, out=None, stream=None) -> torch.Tensor:
-        """y = x W + bias; x [..., K] in the activation dtype, leading dims flattened."""
+        """y = x W + bias; x [..., K] in the activation dtype, leading dims flattened.
+        ``out`` (optional) must be a contiguous [M, N] tensor of that dtype on
+        the layer's device."""
         if self.tiled is None:
             raise RuntimeError("process_weights_after_loading has not run")
+        dt = _TORCH_DTYPE[self.dtype]
+        dev = self.tiled["qweight"].device
+        if x.dtype != dt or x.device != dev or x.shape[-1] != self.K:
+            raise ValueError(f"x must be [..., {self.K}] {dt} on {dev}; got {tuple(x.shape)} {x.dtype} on {x.device}")
+        if bias is not None and (bias.dtype != dt or bias.device != dev or tuple(bias.shape) != (self.N,)
+                                 or not bias.is_contiguous()):
+            raise ValueError(f"bias must be a contiguous [{self.N}] {dt} tensor on {dev}")
         lead = x.shape[:-1]
         x2 = x.reshape(-1, self.K)
         if not x2.is_contiguous():
             x2 = x2.contiguous()
         M = x2.shape[0]
-        y = out if out is not None else torch.empty((M, self.N), dtype=x.dtype, device=x.device)
+        if out is not None and (out.dtype != dt or out.device != dev or tuple(out.shape) != (M, self.N)
+                                or not out.is_contiguous()):
+            raise ValueError(f"out must be a contiguous [{M}, {self.N}] {dt} tensor on {dev}; got "
+                             f"{tuple(out.shape)} {out.dtype} contiguous={out.is_contiguous()}")
+        y = out if out is not None else torch.empty((M, self.N), dtype=dt, device=dev)
         ws_bytes = A.w4_workspace_size(self.layer, M)
-        ws = self._workspace(ws_bytes, x.device) if ws_bytes else None
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        ws = self._workspace(ws_bytes, st) if ws_bytes else None
         t = self.tiled
         A.w4a16_linear(self.layer, M, x2, t["qweight"], t["scales"], t["qzeros"], t["perm"], bias, y, ws, ws_bytes,
-                       stream)
+                       st)
         return y.reshape(*lead, self.N)
 
-    def _workspace(self, nbytes: int, device) -> "torch.Tensor":
-        """A scratch buffer of at least nbytes, kept for later calls."""
-        ws = getattr(self, "_ws", None)
-        if ws is None or ws.numel() < nbytes or ws.device != torch.device(device):
-            ws = torch.empty((nbytes,), dtype=torch.uint8, device=device)
-            self._ws = ws
+    def _workspace(self, nbytes: int, stream) -> "torch.Tensor":
+        """A scratch buffer of at least nbytes for calls on ``stream``: one per
+        stream (calls on different streams may overlap; calls on one stream
+        are ordered), allocated by torch's caching allocator on that stream,
+        so a buffer that is replaced is not reused while the stream still has
+        work on it."""
+        cache = self.__dict__.setdefault("_ws", {})
+        key = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        ws = cache.get(key)
+        if ws is None or ws.numel() < nbytes:
+            if isinstance(stream, torch.cuda.Stream):
+                with torch.cuda.stream(stream):
+                    ws = torch.empty((nbytes,), dtype=torch.uint8, device=stream.device)
+            else:
+                ws = torch.empty((nbytes,), dtype=torch.uint8, device=self.tiled["qweight"].device)
+                ws.record_stream(torch.cuda.ExternalStream(key))
+            cache[key] = ws
         return ws
 
     def dequantize_dense(self, out=None, stream=None) -> torch.Tensor:
