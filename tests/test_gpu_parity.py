@@ -465,7 +465,11 @@ def test_linear_full_size(W, c, M):
 # K = 1152 is nine 128-row blocks, so every pipeline depth runs full trips and
 # a partial tail, and a 4-way split gives uneven K ranges (2, 2, 2, 3).
 WIDE_TILE_SHAPES = [(1024, 16384), (256, 32768), (64, 32768), (32, 32768), (40, 8192), (24, 8192), (200, 8192),
-                    (16, 12288), (9, 20480), (300, 4104), (16, 16392)]
+                    (16, 12288), (9, 20480), (300, 4104), (16, 16392),
+                    # fp16 with >= 256 tiles of 128 x 256: the 32x32x16 kernel, with
+                    # ragged row tiles, a padded half strip and a partial 256-column
+                    # tile
+                    (1100, 8200), (2000, 8192)]
 WIDE_VARIANTS = [
     # (name, fmt, group_size, has_zeros, has_gidx, dtype, K)
     ("awq-fp16-g128", "awq", 128, True, False, "fp16", 1152),
@@ -474,6 +478,7 @@ WIDE_VARIANTS = [
     ("std-bf16-g64-z", "std", 64, True, False, "bf16", 1152),
     ("std-fp16-ch-z", "std", -1, True, False, "fp16", 1152),
     ("std-fp16-g128-z-act", "std", 128, True, True, "fp16", 1152),
+    ("std-fp16-g64-sym", "std", 64, False, False, "fp16", 1152),
     # K tails: nine blocks after padding, the last one partly padding
     ("awq-fp16-g32-z-k1120", "awq", 32, True, False, "fp16", 1120),
     ("std-bf16-ch-sym-k1056", "std", -1, False, False, "bf16", 1056),
@@ -506,8 +511,8 @@ def test_linear_wide_tiles_sampled(W, v):
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,K,gs,act", [(1, 1152, 128, True), (16, 1152, 128, True), (40, 1152, 128, True),
-                                        (300, 1152, 128, True), (1, 1120, 32, False), (40, 1120, 32, False),
-                                        (300, 1120, 32, False)])
+                                        (300, 1152, 128, True), (1100, 1152, 128, True), (1, 1120, 32, False),
+                                        (40, 1120, 32, False), (300, 1120, 32, False), (1100, 1120, 32, False)])
 def test_linear_hip_graph_replays_match_eager(W, M, K, gs, act):
     # act-order (gather into the workspace) and K tails (zero-padded copy
     # into the workspace) inside a captured graph

@@ -91,8 +91,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
                                                              const uint16_t* __restrict__ sc,
                                                              const uint32_t* __restrict__ zs,
                                                              const uint16_t* __restrict__ bias,
-                                                             uint16_t* __restrict__ y, float* __restrict__ part,
-                                                             int64_t M, int64_t K, int64_t N, int G,
+                                                             uint16_t* __restrict__ y, int64_t M, int64_t K,
+                                                             int64_t N, int G,
                                                              int64_t tiles_m, int64_t tiles_n, int64_t group_m) {
   using C = BigCfg<WM, WN, MT, NT, S>;
   constexpr int NP = Groups<GM>::kPeriods;  // scale periods per 128-row block
@@ -119,9 +119,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
   const int c = lane & 31, h = lane >> 5;
   const int64_t T = (N + kTileN - 1) / kTileN;  // strips; the last may be half padding
   const int64_t nblk = K / kTileK;
-  const int64_t split = blockIdx.y, nsplit = gridDim.y;  // split-K ranges of blocks
-  const int64_t kb0 = nblk * split / nsplit;
-  const int64_t nb = nblk * (split + 1) / nsplit - kb0;
+  constexpr int64_t kb0 = 0;  // the whole of K (the issue and pipeline code count blocks from kb0)
+  const int64_t nb = nblk;
   int64_t tm, tn;
   big_tile_of(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
   const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
@@ -251,47 +250,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
 
   // epilogue: element r of lane l is row 8 (r / 4) + 4 h + r % 4 of each row
   // tile, column c of each column tile
-  float* pz = part != nullptr ? part + split * M * N : nullptr;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int64_t n = n0 + (int64_t)(wn * NT + nt) * 32 + c;
     if (n >= N) continue;  // padded columns, or tiles past the last strip
-    const float bv = bias != nullptr && pz == nullptr ? act_to_f32<false>(bias[n]) : 0.f;
+    const float bv = bias != nullptr ? act_to_f32<false>(bias[n]) : 0.f;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + (int64_t)(wm * MT + i) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (m >= M) continue;
-        const float v = acc[i][nt][r] * s_prev[nt];
-        if (pz != nullptr)
-          pz[m * N + n] = v;
-        else
-          y[m * N + n] = f32_to_act<false>(v + bv);
+        y[m * N + n] = f32_to_act<false>(acc[i][nt][r] * s_prev[nt] + bv);
       }
   }
 }
 
-// Launch of one configuration (fp16 only); `group_m` row tiles per band of
-// the tile order.
+// Launch of one configuration (fp16 only, the whole of K per workgroup);
+// `group_m` row tiles per band of the tile order.
 template <int WM, int WN, int MT, int NT, int S, int GM, bool HZ>
 hipError_t run_big(const Args& a, const uint16_t* x, int64_t group_m, hipStream_t st) {
   using C = BigCfg<WM, WN, MT, NT, S>;
   const int64_t Np = (a.N + kTileN - 1) / kTileN * kTileN;
   const int64_t tiles_m = (a.M + C::BM - 1) / C::BM, tiles_n = (Np + C::BN - 1) / C::BN;
-  const int splits = a.splits > 1 ? a.splits : 1;
-  if (splits > 1 && (a.part == nullptr || splits > a.K / kTileK)) return hipErrorInvalidValue;
   if (tiles_m * tiles_n > 0x7FFFFFFF || group_m < 1) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits);
-  gemm_big<WM, WN, MT, NT, S, GM, HZ><<<grid, 64 * WM * WN, 0, st>>>(
-      x, a.qw, a.sc, a.zs, a.bias, a.y, splits > 1 ? a.part : nullptr, a.M, a.K, a.N, a.G, tiles_m, tiles_n,
-      group_m);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
-  const int64_t total4 = a.M * a.N / 4;
-  int64_t blocks = (total4 + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  split_reduce<false><<<(unsigned)blocks, 256, 0, st>>>(a.part, a.bias, a.y, a.M, a.N, splits);
+  gemm_big<WM, WN, MT, NT, S, GM, HZ><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
+      x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N, a.G, tiles_m, tiles_n, group_m);
   return hipGetLastError();
 }
 

@@ -88,6 +88,12 @@ GemmPlan plan_gemm(const Shape& s, int64_t M) {
     } else {
       p = GemmPlan{GemmKind::kSkinny, 1, 1, 8, false, "w4_skinny_k8"};
     }
+  } else if (!s.bf16 && ((M + big_tile_rows() - 1) / big_tile_rows()) *
+                                ((s.Np + big_tile_cols() - 1) / big_tile_cols()) >= 256) {
+    // large M, fp16, at least one 128 x 256 tile of 32x32x16 MFMAs per CU
+    // (with fewer tiles, splitting K measured slower than the wide kernel's
+    // smaller tiles: act-order M = 512 at 8192 x 8192, 94 vs 86 us)
+    p = GemmPlan{GemmKind::kBig, 0, 0, 0, false, "w4_big_128x256"};
   } else {
     // wide kernel: the largest tile that is not taller than M (32 rows at
     // least) and still gives >= 256 workgroups (one per CU), else the
@@ -173,6 +179,16 @@ hipError_t launch_gemm(const Shape& s0, int64_t M, const void* x, const int32_t*
     a.x = xp;
   }
   if (p.kind == GemmKind::kWide) return launch_wide(s, p, a, ws, front, st);
+  if (p.kind == GemmKind::kBig) {
+    const uint16_t* xb = a.x;
+    if (s.has_perm) {
+      uint16_t* xp = static_cast<uint16_t*>(ws);
+      const hipError_t e = launch_gather(a.x, a.perm, xp, a.M, a.K, st);
+      if (e != hipSuccess) return e;
+      xb = xp;
+    }
+    return launch_big(s, M, xb, tiled_w, tiled_s, tiled_z, bias, y, st);
+  }
   Shape sk = s;
   if (s.has_perm) {
     // gather x[:, perm] into the workspace, then run without act-order

@@ -62,7 +62,7 @@ hipError_t launch_tile(const Shape& s, const int32_t* std_w, const int32_t* std_
                        hipStream_t st);
 
 // ---- GEMM (w4_gemm.hip) ----
-enum class GemmKind { kSkinny, kWide };
+enum class GemmKind { kSkinny, kWide, kBig };
 
 struct GemmPlan {
   GemmKind kind;
@@ -81,7 +81,13 @@ hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* 
                        const int32_t* tiled_z, const int32_t* perm, const void* bias, void* y, void* ws,
                        hipStream_t st);
 
-// ---- grouped (mixture-of-experts) GEMM (w4_gemm.hip) ----
+// ---- large-M GEMM on 32x32x16 MFMA tiles, fp16 (w4_big.hip) ----
+int64_t big_tile_rows();
+int64_t big_tile_cols();
+hipError_t launch_big(const Shape& s, int64_t M, const uint16_t* x, const int32_t* tiled_w, const void* tiled_s,
+                      const int32_t* tiled_z, const void* bias, void* y, hipStream_t st);
+
+// ---- grouped (mixture-of-experts) GEMM (w4_moe.hip) ----
 GemmPlan plan_moe(const Shape& s, int64_t max_rows, int experts);
 hipError_t launch_moe(const Shape& s, int experts, int64_t total_rows, int64_t max_rows, const void* x,
                       const int32_t* offsets, const int32_t* tiled_w, const void* tiled_s, const int32_t* tiled_z,
