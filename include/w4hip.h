@@ -177,6 +177,26 @@ w4_status w4a16_linear(const w4_layer* layer, int64_t M, const void* x, const in
                        const void* tiled_scales, const int32_t* tiled_qzeros, const int32_t* perm,
                        const void* bias, void* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* w4a16_linear for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, result and accuracy as w4a16_linear without the workspace
+ * pair: the workspace is a static device array of
+ * w4_noalloc_scratch_bytes() bytes (64 MiB), one per device, held until the
+ * process ends.  The call allocates nothing; its first call on a device
+ * resolves that device's array address (hipGetSymbolAddress) with the device
+ * current, so make the first call outside graph capture.
+ *   W4_ERR_WORKSPACE  the call needs more than w4_noalloc_scratch_bytes()
+ *                     (w4_workspace_size() tells how much it needs)
+ * Every call on a device shares that device's array, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that overlap
+ * in time on one device race, whatever their streams. */
+w4_status w4a16_linear_noalloc(const w4_layer* layer, int64_t M, const void* x, const int32_t* tiled_qweight,
+                               const void* tiled_scales, const int32_t* tiled_qzeros, const int32_t* perm,
+                               const void* bias, void* y, void* stream);
+
+/* Bytes of the static workspace array of w4a16_linear_noalloc.  Host only. */
+size_t w4_noalloc_scratch_bytes(void);
+
 /* Grouped W4A16 linear for mixture-of-experts layers (the WNA16 MoE path of
  * the vLLM AWQ practice page, section 5.4, and of the SGLang quantization
  * page's MoE section): num_experts experts share one w4_layer description

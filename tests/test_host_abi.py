@@ -26,7 +26,7 @@ def W():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:w4_status|const\s+char\s*\*)\s*(w4\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:w4_status|const\s+char\s*\*|size_t)\s*(w4\w+)\s*\(", text, flags=re.M)
 
 
 def test_header_declares_the_lifecycle_calls():
@@ -176,3 +176,27 @@ def test_moe_rejects_k_tails_and_act_order(W):
     for L in (W.make_layer(320, 256, 64, True, False, "fp16"), W.make_layer(512, 256, 128, True, True, "fp16")):
         st = W.lib().w4a16_moe_linear(ctypes.byref(L), 2, 8, 4, 16, 16, 16, 16, 16, None, 16, None)
         assert st == W.W4_ERR_UNSUPPORTED
+
+
+def test_noalloc_linear_rejects_before_any_launch(W):
+    # the static workspace bounds what a no-allocation call can run; every
+    # refusal happens on the host
+    lib = W.lib()
+    assert W.w4_noalloc_scratch_bytes() == 64 << 20
+
+    def na(L, M, x=16, qw=16, sc=16, qz=16, perm=None, bias=None, y=16):
+        return lib.w4a16_linear_noalloc(ctypes.byref(L), M, x, qw, sc, qz, perm, bias, y, None)
+
+    L = W.make_layer(512, 256, 128, True, False, "fp16")
+    assert na(L, -1) == W.W4_ERR_INVALID_ARGUMENT
+    assert na(L, 1, x=None) == W.W4_ERR_INVALID_ARGUMENT
+    assert na(L, 1, y=18) == W.W4_ERR_INVALID_ARGUMENT
+    assert na(L, 0) == W.W4_OK
+    # act-order at M = 8192, K = 8192 needs a 128 MiB gather: over the limit
+    La = W.make_layer(8192, 8192, 128, True, True, "fp16")
+    assert W.w4_workspace_size(La, 8192) > W.w4_noalloc_scratch_bytes()
+    assert na(La, 8192, perm=16) == W.W4_ERR_WORKSPACE
+    # every mid-batch split-K workspace fits
+    for K, N in ((8192, 10240), (8192, 8192), (28672, 8192)):
+        for M in (32, 64, 128, 256):
+            assert W.w4_workspace_size(W.make_layer(K, N, 128, False, False, "bf16"), M) <= W.w4_noalloc_scratch_bytes()

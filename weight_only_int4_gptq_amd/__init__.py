@@ -11,6 +11,7 @@ from ._abi import (  # noqa: F401
     W4_FP16, W4_BF16, w4_layer, w4_sizes_t, make_layer, lib,
     w4_check_layer, w4_sizes, w4_workspace_size, w4_kernel_name, w4_status_str,
     w4_repack_awq, w4_repack_gptq, w4a16_linear, w4_dequant_dense, w4a16_moe_linear,
+    w4a16_linear_noalloc, w4_noalloc_scratch_bytes,
 )
 
 

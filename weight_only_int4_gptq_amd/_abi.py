@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
             "w4_dequant_dense": ([P(w4_layer), VP, VP, VP, VP, VP, VP], ctypes.c_int),
             "w4a16_moe_linear": ([P(w4_layer), ctypes.c_int32, I64, I64, VP, VP, VP, VP, VP, VP, VP, VP],
                                  ctypes.c_int),
+            "w4a16_linear_noalloc": ([P(w4_layer), I64, VP, VP, VP, VP, VP, VP, VP, VP], ctypes.c_int),
+            "w4_noalloc_scratch_bytes": ([], SZ),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -156,3 +158,14 @@ def w4a16_moe_linear(layer, num_experts, total_rows, max_rows, x, expert_offsets
     _raise("w4a16_moe_linear", lib().w4a16_moe_linear(
         ctypes.byref(layer), int(num_experts), int(total_rows), int(max_rows), _ptr(x), _ptr(expert_offsets),
         _ptr(tiled_qweight), _ptr(tiled_scales), _ptr(tiled_qzeros), _ptr(bias), _ptr(y), _stream(stream)))
+
+
+def w4a16_linear_noalloc(layer, M, x, tiled_qweight, tiled_scales, tiled_qzeros, perm, bias, y, stream=None) -> None:
+    """w4a16_linear with the library's static device workspace (allocates nothing)."""
+    _raise("w4a16_linear_noalloc", lib().w4a16_linear_noalloc(
+        ctypes.byref(layer), int(M), _ptr(x), _ptr(tiled_qweight), _ptr(tiled_scales), _ptr(tiled_qzeros),
+        _ptr(perm), _ptr(bias), _ptr(y), _stream(stream)))
+
+
+def w4_noalloc_scratch_bytes() -> int:
+    return int(lib().w4_noalloc_scratch_bytes())

@@ -15,6 +15,13 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 // Device check (gfx950 only), cached per device ordinal.
 std::atomic<int> g_dev_state[64];  // 0 unknown, 1 gfx950, 2 other
 
+constexpr int64_t kMaxDim = int64_t(1) << 20;
+constexpr int64_t kMaxM = int64_t(1) << 24;
+
+}  // namespace
+
+namespace w4 {
+
 w4_status device_status() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return W4_ERR_HIP;
@@ -30,10 +37,25 @@ w4_status device_status() {
   return ok ? W4_OK : W4_ERR_UNSUPPORTED;
 }
 
-constexpr int64_t kMaxDim = int64_t(1) << 20;
-constexpr int64_t kMaxM = int64_t(1) << 24;
+w4_status linear_checks(const w4_layer* L, int64_t M, const void* x, const int32_t* tiled_qweight,
+                        const void* tiled_scales, const int32_t* tiled_qzeros, const int32_t* perm, const void* bias,
+                        const void* y) {
+  const w4_status st = w4_check_layer(L);
+  if (st != W4_OK) return st;
+  if (M < 0) return W4_ERR_INVALID_ARGUMENT;
+  if (M > kMaxM) return W4_ERR_UNSUPPORTED;
+  const Shape s = shape_of(L);
+  if (!x || !tiled_qweight || !tiled_scales || !y) return W4_ERR_INVALID_ARGUMENT;
+  if (s.has_z != (tiled_qzeros != nullptr) || s.has_perm != (perm != nullptr)) return W4_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(tiled_qweight, 16) || !aligned(tiled_scales, 2) || !aligned(y, 4) ||
+      (bias && !aligned(bias, 2)) || (tiled_qzeros && !aligned(tiled_qzeros, 4)) || (perm && !aligned(perm, 16)))
+    return W4_ERR_INVALID_ARGUMENT;
+  return W4_OK;
+}
 
-}  // namespace
+}  // namespace w4
+
+using w4::device_status;
 
 extern "C" {
 
@@ -144,21 +166,13 @@ w4_status w4_repack_gptq(const w4_layer* L, const int32_t* std_qweight, const in
 w4_status w4a16_linear(const w4_layer* L, int64_t M, const void* x, const int32_t* tiled_qweight,
                        const void* tiled_scales, const int32_t* tiled_qzeros, const int32_t* perm, const void* bias,
                        void* y, void* workspace, size_t workspace_bytes, void* stream) {
-  w4_status st = w4_check_layer(L);
-  if (st != W4_OK) return st;
-  if (M < 0) return W4_ERR_INVALID_ARGUMENT;
-  if (M > kMaxM) return W4_ERR_UNSUPPORTED;
+  w4_status st = w4::linear_checks(L, M, x, tiled_qweight, tiled_scales, tiled_qzeros, perm, bias, y);
+  if (st != W4_OK || M == 0) return st;
   const Shape s = w4::shape_of(L);
-  if (!x || !tiled_qweight || !tiled_scales || !y) return W4_ERR_INVALID_ARGUMENT;
-  if (s.has_z != (tiled_qzeros != nullptr) || s.has_perm != (perm != nullptr)) return W4_ERR_INVALID_ARGUMENT;
-  if (!aligned(x, 16) || !aligned(tiled_qweight, 16) || !aligned(tiled_scales, 2) || !aligned(y, 4) ||
-      (bias && !aligned(bias, 2)) || (tiled_qzeros && !aligned(tiled_qzeros, 4)) || (perm && !aligned(perm, 16)))
-    return W4_ERR_INVALID_ARGUMENT;
-  if (M == 0) return W4_OK;
   const size_t need = w4::gemm_workspace_bytes(s, M);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return W4_ERR_WORKSPACE;
   if (workspace != nullptr && !aligned(workspace, 16)) return W4_ERR_INVALID_ARGUMENT;
-  st = device_status();
+  st = w4::device_status();
   if (st != W4_OK) return st;
   if (w4::launch_gemm(s, M, x, tiled_qweight, tiled_scales, tiled_qzeros, perm, bias, y, workspace,
                       static_cast<hipStream_t>(stream)) != hipSuccess)

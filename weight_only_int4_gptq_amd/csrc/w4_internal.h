@@ -51,6 +51,13 @@ inline Shape padded_k(const Shape& s) {
   return p;
 }
 
+// ---- host-side checks shared by the entry points (w4_api.cpp) ----
+w4_status device_status();  // W4_OK on a gfx950 device, cached per device
+// argument checks of a linear call (descriptor, M, pointers, alignment)
+w4_status linear_checks(const w4_layer* L, int64_t M, const void* x, const int32_t* tiled_qweight,
+                        const void* tiled_scales, const int32_t* tiled_qzeros, const int32_t* perm, const void* bias,
+                        const void* y);
+
 // ---- repack launchers (w4_repack.hip) ----
 hipError_t launch_awq_to_std(const Shape& s, const int32_t* awq_w, const int32_t* awq_z, int32_t* std_w,
                              int32_t* std_z, hipStream_t st);
