@@ -10,3 +10,4 @@ method's arithmetic).
 See ``oracle/w4_oracle.py`` for the functions and the passages they follow.
 """
 from .w4_oracle import *  # noqa: F401,F403
+from .w4a8_oracle import *  # noqa: F401,F403
