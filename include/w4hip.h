@@ -228,6 +228,57 @@ w4_status w4a16_moe_linear(const w4_layer* layer, int32_t num_experts, int64_t t
                            const void* tiled_scales, const int32_t* tiled_qzeros, const void* bias, void* y,
                            void* stream);
 
+/* ---- INT4 weights x FP8 activations (W4A8-fp8) ----
+ * The W4AFp8 scheme of the SGLang quantization page (section 5: int4
+ * weights, one scale per group of 128, fp8 activations with a static input
+ * scale) and the fp8-activation branch of the vLLM loading page ("Boundaries
+ * and failures": weights preprocessed for float8_e4m3fn activations, scales
+ * times 512).  The weights are the tiled buffers of w4_repack_gptq (group
+ * size 128 or -1; 32 and 64 return W4_ERR_UNSUPPORTED); the activations are
+ * quantized per tensor:
+ *   x_q = e4m3(clamp(x / s_x, -448, 448)),  x / s_x in fp32, round to
+ *         nearest even, E4M3 = float8_e4m3fn (bias 7, largest 448)
+ *   y   = s_x * x_q W + bias,  W[k][n] = (q - z) s as for w4a16_linear
+ * computed with the fp8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): a 4-bit
+ * code written into a byte is the E4M3 value code / 512, and the MFMA's
+ * power-of-two block scale of the weight operand restores the 512 exactly. */
+
+/* Quantize activations x [M][K] (act dtype, device) with the scale
+ * x_scale[0] (fp32, device) into
+ *   xq      uint8 [M][Kp] (device, 8-byte aligned): E4M3 codes in operand
+ *           order: byte 32 q + 8 j + i of 128-byte block b of row m holds
+ *           column 128 b + 32 j + 8 q + [0,4,1,5,2,6,3,7][i] of the row
+ *           (with act-order: column perm[that index] of x); columns K .. Kp-1
+ *           hold 0;
+ *   rowsum  fp32 [Kp/128][Mr] (device), Mr = M rounded up to a multiple of
+ *           4: the sum of the E4M3 values of each row's 128-column block
+ *           (rows M .. Mr-1 hold 0).
+ * perm: the act-order permutation written by w4_repack_gptq (NULL iff
+ * !has_g_idx).  Asynchronous on `stream`. */
+w4_status w4a8_quantize(const w4_layer* layer, int64_t M, const void* x, const float* x_scale, const int32_t* perm,
+                        uint8_t* xq, float* rowsum, void* stream);
+
+/* Bytes of workspace w4a8_linear needs for M rows (xq and rowsum above).
+ * Host only. */
+w4_status w4a8_workspace_size(const w4_layer* layer, int64_t M, size_t* bytes);
+
+/* y [M][N] (act dtype) = s_x x_q W + bias for activations x [M][K] (act
+ * dtype) and the per-tensor scale x_scale[0] (fp32, device): w4a8_quantize
+ * into the workspace, then the fused int4 x fp8 GEMM.  Arguments as for
+ * w4a16_linear; workspace >= w4a8_workspace_size() bytes (16-byte aligned,
+ * no initialization needed).  fp32 accumulation, y rounded once.  Accuracy:
+ * within max|y - ref| <= 1e-2 (1 + |ref|) elementwise and relative
+ * Frobenius error <= 2e-3 of the float64 result of the same quantized
+ * activations (the oracle's reference_w4a8_linear). */
+w4_status w4a8_linear(const w4_layer* layer, int64_t M, const void* x, const float* x_scale,
+                      const int32_t* tiled_qweight, const void* tiled_scales, const int32_t* tiled_qzeros,
+                      const int32_t* perm, const void* bias, void* y, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Name of the kernel w4a8_linear launches for M rows ("invalid" for a bad
+ * or unsupported descriptor).  Static string; host only. */
+const char* w4a8_kernel_name(const w4_layer* layer, int64_t M);
+
 /* Dense dequantization (the unfused path the fused GEMM is measured against).
  * The vLLM AWQ practice page (section 5.3) runs large batches as "dequantize,
  * then matmul" instead of the fused kernel; this call is the first half of

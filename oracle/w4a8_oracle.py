@@ -38,7 +38,8 @@ from .w4_oracle import act_to_f64, codes_from_inputs, dequant, group_index, line
 
 E4M3_MAX = 448.0
 
-__all__ = ["E4M3_MAX", "e4m3_to_f64", "e4m3_rne", "quantize_acts_fp8", "reference_w4a8_linear"]
+__all__ = ["E4M3_MAX", "e4m3_to_f64", "e4m3_rne", "quantize_acts_fp8", "reference_w4a8_linear",
+           "FP8_BYTE_OFFSETS", "fp8_operand_order", "fp8_block_sums"]
 
 
 def e4m3_to_f64(codes) -> np.ndarray:
@@ -98,3 +99,41 @@ def reference_w4a8_linear(x, fmt, dtype, qweight, qzeros, scales, group_size, x_
     W = dequant(q, z, act_to_f64(scales, dtype), group_index(K, group_size, g_idx))
     b = None if bias is None else act_to_f64(bias, dtype)
     return linear_ref(xq, W, b)
+
+
+# ----------------------------------------------------------------------------
+# The library's layout of quantized activations (its own format, like the
+# tile layout of the weights): within each 128-column block of a row, byte
+# 32 q + 8 j + i holds column 32 j + 8 q + FP8_BYTE_OFFSETS[i].
+# ----------------------------------------------------------------------------
+
+FP8_BYTE_OFFSETS = (0, 4, 1, 5, 2, 6, 3, 7)
+
+
+def fp8_operand_order(codes, Kp: int) -> np.ndarray:
+    """Codes [M][K] (sorted column order) -> bytes [M][Kp] in operand order,
+    columns K .. Kp - 1 zero."""
+    c = np.asarray(codes, dtype=np.uint8)
+    M, K = c.shape
+    assert Kp % 128 == 0 and Kp >= K
+    src = np.zeros((M, Kp), dtype=np.uint8)
+    src[:, :K] = c
+    out = np.zeros((M, Kp), dtype=np.uint8)
+    for b in range(Kp // 128):
+        for q in range(4):
+            for j in range(4):
+                for i in range(8):
+                    out[:, 128 * b + 32 * q + 8 * j + i] = src[:, 128 * b + 32 * j + 8 * q + FP8_BYTE_OFFSETS[i]]
+    return out
+
+
+def fp8_block_sums(codes, Kp: int) -> np.ndarray:
+    """Sums of the E4M3 values of each 128-column block of each row (sorted
+    order), [Kp / 128][Mr] with Mr = M rounded up to 4 (extra rows zero)."""
+    v = e4m3_to_f64(np.asarray(codes, dtype=np.uint8))
+    M, K = v.shape
+    Mr = (M + 3) // 4 * 4
+    out = np.zeros((Kp // 128, Mr), dtype=np.float64)
+    for b in range(Kp // 128):
+        out[b, :M] = v[:, 128 * b:min(128 * (b + 1), K)].sum(axis=1)
+    return out

@@ -167,3 +167,34 @@ def test_mutation_wrong_exponent_bias_is_caught(monkeypatch):
     monkeypatch.setattr(O, "e4m3_to_f64", bias8)
     with pytest.raises(AssertionError):
         test_e4m3_golden_values()
+
+
+def test_operand_order_worked_bytes_and_bijection():
+    # column -> byte, derived by hand from "byte 32 q + 8 j + i holds column
+    # 32 j + 8 q + [0,4,1,5,2,6,3,7][i]": column 1 is offset 1 = entry 2 of
+    # the list with j = q = 0, so byte 2; column 4 -> byte 1; column 8 (q = 1)
+    # -> byte 32; column 32 (j = 1) -> byte 8; column 127 (j = 3, q = 3,
+    # offset 7 = entry 7) -> byte 127; column 130 -> block 1, byte 128 + 4
+    K = 256
+    expect = {1: 2, 4: 1, 8: 32, 32: 8, 127: 127, 130: 132, 0: 0}
+    for col, byte in expect.items():
+        codes = np.zeros((1, K), dtype=np.uint8)
+        codes[0, col] = 0x38
+        out = O.fp8_operand_order(codes, K)
+        assert out[0, byte] == 0x38 and out.sum() == 0x38, (col, byte)
+    # a permutation of each block (every byte used once)
+    codes = (np.arange(256) % 251).astype(np.uint8)[None, :]
+    out = O.fp8_operand_order(codes, 256)
+    assert sorted(out[0].tolist()) == sorted(codes[0].tolist())
+    # K tail: the padded columns are zero
+    out = O.fp8_operand_order(np.full((2, 96), 0x38, dtype=np.uint8), 128)
+    assert int((out != 0).sum()) == 2 * 96
+
+
+def test_block_sums_closed_form():
+    codes = np.full((3, 256), 0x38, dtype=np.uint8)       # every value 1.0
+    codes[1, 128:] = 0xB8                                  # -1.0
+    s = O.fp8_block_sums(codes, 256)
+    assert s.shape == (2, 4)
+    assert s[:, :3].tolist() == [[128.0, 128.0, 128.0], [128.0, -128.0, 128.0]]
+    assert (s[:, 3] == 0).all()

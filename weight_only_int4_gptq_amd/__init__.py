@@ -12,6 +12,7 @@ from ._abi import (  # noqa: F401
     w4_check_layer, w4_sizes, w4_workspace_size, w4_kernel_name, w4_status_str,
     w4_repack_awq, w4_repack_gptq, w4a16_linear, w4_dequant_dense, w4a16_moe_linear,
     w4a16_linear_noalloc, w4_noalloc_scratch_bytes,
+    w4a8_quantize, w4a8_workspace_size, w4a8_linear, w4a8_kernel_name,
 )
 
 

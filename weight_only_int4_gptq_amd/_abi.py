@@ -69,6 +69,10 @@ def lib() -> ctypes.CDLL:
             "w4a16_moe_linear": ([P(w4_layer), ctypes.c_int32, I64, I64, VP, VP, VP, VP, VP, VP, VP, VP],
                                  ctypes.c_int),
             "w4a16_linear_noalloc": ([P(w4_layer), I64, VP, VP, VP, VP, VP, VP, VP, VP], ctypes.c_int),
+            "w4a8_quantize": ([P(w4_layer), I64, VP, VP, VP, VP, VP, VP], ctypes.c_int),
+            "w4a8_workspace_size": ([P(w4_layer), I64, P(SZ)], ctypes.c_int),
+            "w4a8_linear": ([P(w4_layer), I64, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP], ctypes.c_int),
+            "w4a8_kernel_name": ([P(w4_layer), I64], ctypes.c_char_p),
             "w4_noalloc_scratch_bytes": ([], SZ),
         }
         for name, (args, res) in sig.items():
@@ -169,3 +173,27 @@ def w4a16_linear_noalloc(layer, M, x, tiled_qweight, tiled_scales, tiled_qzeros,
 
 def w4_noalloc_scratch_bytes() -> int:
     return int(lib().w4_noalloc_scratch_bytes())
+
+
+def w4a8_quantize(layer, M, x, x_scale, perm, xq, rowsum, stream=None) -> None:
+    """E4M3 activations in operand order and their 128-column block sums."""
+    _raise("w4a8_quantize", lib().w4a8_quantize(ctypes.byref(layer), int(M), _ptr(x), _ptr(x_scale), _ptr(perm),
+                                                _ptr(xq), _ptr(rowsum), _stream(stream)))
+
+
+def w4a8_workspace_size(layer, M) -> int:
+    b = ctypes.c_size_t(0)
+    _raise("w4a8_workspace_size", lib().w4a8_workspace_size(ctypes.byref(layer), int(M), ctypes.byref(b)))
+    return int(b.value)
+
+
+def w4a8_linear(layer, M, x, x_scale, tiled_qweight, tiled_scales, tiled_qzeros, perm, bias, y, workspace,
+                workspace_bytes, stream=None) -> None:
+    """INT4 weights x FP8 activations (static per-tensor scale x_scale[0])."""
+    _raise("w4a8_linear", lib().w4a8_linear(
+        ctypes.byref(layer), int(M), _ptr(x), _ptr(x_scale), _ptr(tiled_qweight), _ptr(tiled_scales),
+        _ptr(tiled_qzeros), _ptr(perm), _ptr(bias), _ptr(y), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def w4a8_kernel_name(layer, M) -> str:
+    return lib().w4a8_kernel_name(ctypes.byref(layer), int(M)).decode()

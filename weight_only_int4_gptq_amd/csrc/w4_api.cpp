@@ -223,4 +223,78 @@ w4_status w4_dequant_dense(const w4_layer* L, const int32_t* tiled_qweight, cons
   return W4_OK;
 }
 
+// ---- INT4 weights x FP8 activations ----
+
+namespace {
+w4_status w4a8_layer_ok(const w4_layer* L) {
+  const w4_status st = w4_check_layer(L);
+  if (st != W4_OK) return st;
+  // one MFMA step covers 128 rows: one group of 128, or any number of
+  // blocks of a per-channel layer
+  if (L->group_size != 128 && L->group_size != -1) return W4_ERR_UNSUPPORTED;
+  return W4_OK;
+}
+}  // namespace
+
+w4_status w4a8_workspace_size(const w4_layer* L, int64_t M, size_t* bytes) {
+  const w4_status st = w4a8_layer_ok(L);
+  if (st != W4_OK) return st;
+  if (bytes == nullptr || M < 0) return W4_ERR_INVALID_ARGUMENT;
+  if (M > kMaxM) return W4_ERR_UNSUPPORTED;
+  *bytes = M == 0 ? 0 : w4::f8_workspace_bytes(w4::padded_k(w4::shape_of(L)), M);
+  return W4_OK;
+}
+
+w4_status w4a8_quantize(const w4_layer* L, int64_t M, const void* x, const float* x_scale, const int32_t* perm,
+                        uint8_t* xq, float* rowsum, void* stream) {
+  w4_status st = w4a8_layer_ok(L);
+  if (st != W4_OK) return st;
+  if (M < 0) return W4_ERR_INVALID_ARGUMENT;
+  if (M > kMaxM) return W4_ERR_UNSUPPORTED;
+  const Shape s = w4::shape_of(L);
+  if (!x || !x_scale || !xq || !rowsum) return W4_ERR_INVALID_ARGUMENT;
+  if (s.has_perm != (perm != nullptr)) return W4_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 2) || !aligned(x_scale, 4) || !aligned(xq, 8) || !aligned(rowsum, 4) || (perm && !aligned(perm, 4)))
+    return W4_ERR_INVALID_ARGUMENT;
+  if (M == 0) return W4_OK;
+  st = device_status();
+  if (st != W4_OK) return st;
+  if (w4::launch_f8_quantize(s, M, x, x_scale, perm, xq, rowsum, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return W4_ERR_HIP;
+  return W4_OK;
+}
+
+w4_status w4a8_linear(const w4_layer* L, int64_t M, const void* x, const float* x_scale,
+                      const int32_t* tiled_qweight, const void* tiled_scales, const int32_t* tiled_qzeros,
+                      const int32_t* perm, const void* bias, void* y, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  w4_status st = w4a8_layer_ok(L);
+  if (st != W4_OK) return st;
+  st = w4::linear_checks(L, M, x, tiled_qweight, tiled_scales, tiled_qzeros, perm, bias, y);
+  if (st != W4_OK || M == 0) return st;
+  if (x_scale == nullptr || !aligned(x_scale, 4)) return W4_ERR_INVALID_ARGUMENT;
+  const Shape s0 = w4::shape_of(L);
+  const Shape s = w4::padded_k(s0);
+  const size_t need = w4::f8_workspace_bytes(s, M);
+  if (workspace == nullptr || workspace_bytes < need) return W4_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return W4_ERR_INVALID_ARGUMENT;
+  st = device_status();
+  if (st != W4_OK) return st;
+  uint8_t* xq = static_cast<uint8_t*>(workspace);
+  float* rs = reinterpret_cast<float*>(xq + w4::f8_xq_bytes(s, M));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (w4::launch_f8_quantize(s0, M, x, x_scale, perm, xq, rs, hs) != hipSuccess) return W4_ERR_HIP;
+  if (w4::launch_f8_gemm(s, M, xq, rs, x_scale, tiled_qweight, tiled_scales, tiled_qzeros, bias, y, hs) !=
+      hipSuccess)
+    return W4_ERR_HIP;
+  return W4_OK;
+}
+
+const char* w4a8_kernel_name(const w4_layer* L, int64_t M) {
+  if (w4a8_layer_ok(L) != W4_OK || M < 0 || M > kMaxM) return "invalid";
+  if (M == 0) return "none";
+  return w4::f8_kernel_name(M);
+}
+
 }  // extern "C"

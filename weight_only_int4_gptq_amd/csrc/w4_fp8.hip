@@ -1,0 +1,379 @@
+// INT4 weights x FP8 activations (W4A8-fp8) on gfx950.
+//
+// y = s_x * x_q W + bias, x_q = e4m3(clamp(x / s_x, +-448)) with a static
+// per-tensor activation scale s_x, W[k, n] = (q - z[g(k), n]) s[g(k), n]
+// (the W4AFp8 scheme of the SGLang quantization page, section 5, and the
+// fp8-activation branch of the vLLM loading page, "Boundaries and failures").
+//
+// The weights keep the library's tile layout.  A 4-bit code written into a
+// byte is the E4M3 value code * 2^-9 (codes 0..7 are the subnormals m 2^-9,
+// 8..15 the exponent-1 values), so the B operand of the fp8 MFMA is the
+// nibbles themselves, unpacked with two masks and a shift, and the MFMA's
+// E8M0 scale of B (2^9) multiplies them back exactly: the 512 the pages
+// apply to the scales.  The zero point is removed per group with the row
+// sums of the quantized activations: the period sum of x_q (q - z) is
+// P - z RS, with P the MFMA result and RS the row sum.
+//
+// v_mfma_scale_f32_16x16x128_f8f6f4 consumes 128 K values per instruction,
+// exactly one group of 128 rows, so each block's product is one MFMA per
+// 16 x 16 tile, folded into the fp32 total with the group's scale; per-channel
+// layers accumulate all blocks in the MFMA and scale once.  Lane l supplies
+// row (A) or column (B) l % 16 and 32 K values; lane l's B operand is its
+// 16-byte chunk of the tile layout (column l % 16 at rows 32 j + 8 (l / 16) + e
+// of the block, j = 0..3, K-offset e in nibble slot S[e], S = [0,4,1,5,2,6,3,7]),
+// so the activations are quantized straight into that order ("operand
+// order"): byte 32 q + 8 j + i of a 128-byte block holds column
+// 32 j + 8 q + S[i] of the block.
+#include "w4_kern.h"
+
+namespace w4 {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+constexpr int kE8m0One = 127;       // 2^0
+constexpr int kE8m0Code = 127 + 9;  // 2^9: a code byte is worth code * 2^-9
+
+__device__ __forceinline__ f4 mfma_f8(const v8i& a, const v8i& b, f4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kE8m0One, 0, kE8m0Code);
+}
+
+// E4M3 value of a byte (finite bytes only), for the row sums
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t e = (b >> 3) & 0xF, m = b & 7;
+  const float mag = e == 0 ? (float)m * 0.001953125f : __builtin_ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
+  return (b & 0x80) ? -mag : mag;
+}
+
+// ---------------------------------------------------------------------------
+// Activation quantization: one thread per 8 consecutive (sorted) columns.
+// xq [M][Kp] in operand order; rs [Kp/128][Mr] fp32 block sums of the
+// quantized values (the exact E4M3 values summed in fp32), Mr = M rounded up
+// to a multiple of 4 (rows M .. Mr - 1 are zero); columns K .. Kp - 1 of a
+// K tail are zero.
+// ---------------------------------------------------------------------------
+template <bool BF16, bool PERM>
+__global__ void quant_fp8(const uint16_t* __restrict__ x, const float* __restrict__ xscale,
+                          const int32_t* __restrict__ perm, uint8_t* __restrict__ xq, float* __restrict__ rs,
+                          int64_t M, int64_t Mr, int64_t K, int64_t Kp) {
+  const int64_t chunks = Kp / 8;  // per row; 16 per 128-column block
+  const int64_t total = Mr * chunks;  // a multiple of 16
+  const float s = xscale[0];
+  // 16 consecutive threads cover one block of one row and leave the loop
+  // together, so the block sum reduces inside a 16-lane group of a wave
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = idx / chunks, cc = idx - m * chunks;
+    const int64_t k0 = 8 * cc;
+    const uint16_t* row = x + m * K;
+    uint32_t codes[8];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // column k0 + S[i] of the sorted order, S = [0,4,1,5,2,6,3,7]
+      const int64_t k = k0 + ((i & 1) ? 4 + (i >> 1) : (i >> 1));
+      float v = 0.f;
+      if (m < M && k < K) {
+        const uint32_t src = PERM ? (uint32_t)perm[k] : (uint32_t)k;
+        v = act_to_f32<BF16>(row[src < (uint32_t)K ? src : 0u]) / s;  // IEEE fp32 division
+      }
+      v = __builtin_fminf(__builtin_fmaxf(v, -448.f), 448.f);
+      codes[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false) & 0xFFu;
+      sum += e4m3_value(codes[i]);
+    }
+    // operand order: chunk cc of its block -> (j, q) = (cc % 16 / 4, cc % 4)
+    const int64_t b = cc / 16, c16 = cc % 16;
+    if (m < M) {
+      const uint32_t lo = codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24);
+      const uint32_t hi = codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24);
+      *reinterpret_cast<uint2*>(xq + m * Kp + 128 * b + 32 * (c16 % 4) + 8 * (c16 / 4)) = make_uint2(lo, hi);
+    }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) sum += __shfl_xor(sum, d, 16);
+    if (c16 == 0) rs[b * Mr + m] = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused GEMM: WN waves side by side, each MT 16-row tiles x NS strips
+// (workgroup tile 16 MT x 16 NS WN); K walked in 128-row blocks through an
+// S-deep pipeline as in the wide kernel: the BM x 128-byte activation tile
+// of block b in LDS slot b % S (direct global->LDS loads; 16-byte chunk c of
+// row r at position c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), so the 16
+// rows one A read touches fall on distinct banks), the packed words, scales,
+// zero words and row sums of block b in register slot b % S.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int MT, int NS, int WN, int S>
+struct F8Cfg {
+  static constexpr int BM = 16 * MT;
+  static constexpr int BN = 16 * NS * WN;
+  static constexpr int NA = BM * 128 / (1024 * WN);  // 1 KiB direct-to-LDS loads per wave per block
+  static constexpr int kAfter = (S - 2) * (NS + NA);
+  static_assert(NA >= 1 && NA * 1024 * WN == BM * 128, "the activation tile splits evenly over the waves");
+  static_assert(S >= 2 && S <= 4 && kAfter < 64, "pipeline depth");
+};
+
+template <int MT, int NS, int WN, int S, bool PERCH, bool HAS_Z, bool BF16>
+__global__ __launch_bounds__(64 * WN, 1) void gemm_f8(const uint8_t* __restrict__ xq, const float* __restrict__ rs,
+                                                       const float* __restrict__ xscale,
+                                                       const u4* __restrict__ qw, const uint16_t* __restrict__ sc,
+                                                       const uint32_t* __restrict__ zs,
+                                                       const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
+                                                       int64_t M, int64_t Mr, int64_t K, int64_t N, int G) {
+  using C = F8Cfg<MT, NS, WN, S>;
+  constexpr int NA = C::NA;
+  constexpr int kSlot = C::BM * 128, kNone = 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kSlot];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kSlot];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[S > 2 ? kSlot : kNone];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds3[S > 3 ? kSlot : kNone];
+  auto slot_lds = [&](int u) __attribute__((always_inline)) -> uint8_t* {
+    switch (u) {
+      case 0: return lds0;
+      case 1: return lds1;
+      case 2: return lds2;
+      default: return lds3;
+    }
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, quad = lane >> 4;
+  const int64_t T = (N + kTileN - 1) / kTileN;
+  const int64_t nblk = K / kTileK;
+  const int64_t m0 = (int64_t)blockIdx.y * C::BM;
+  const int64_t tw0 = ((int64_t)blockIdx.x * WN + wave) * NS;
+  const uint32_t zshift = 4u * (uint32_t)(c & 7);
+
+  const u4* wp[NS];
+  const uint16_t* sp[NS];
+  const uint32_t* zp[NS];
+#pragma unroll
+  for (int nt = 0; nt < NS; ++nt) {
+    const int64_t t = tw0 + nt;
+    const int64_t tt = t < T ? t : 0;
+    wp[nt] = qw + tt * nblk * 64 + lane;
+    sp[nt] = sc + tt * G * kTileN + c;
+    zp[nt] = HAS_Z ? zs + tt * G * 2 + (c >> 3) : nullptr;
+  }
+  // staging: load i of this wave fills rows 8 (NA wave + i) .. + 7; lane l
+  // lands at position l % 8 of row base + l / 8 and so loads logical chunk
+  // (l % 8) ^ swz(row)
+  const uint8_t* ap[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int row = 8 * (NA * wave + i) + (lane >> 3);
+    int64_t m = m0 + row;
+    m = m < M ? m : M - 1;
+    ap[i] = xq + m * K + 16 * ((lane & 7) ^ swz8(row));
+  }
+  // the lane's four output rows of tile i: 16 i + 4 quad + 0..3 (their block
+  // sums are one 16-byte load; groups of rows past Mr, never stored, read
+  // the last group)
+  const float* rp[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int64_t r = m0 + 16 * i + 4 * quad;
+    rp[i] = rs + (r < Mr ? r : Mr - 4);
+  }
+
+  struct Slot {
+    u4 w[NS];
+    uint16_t s[NS];
+    uint32_t z[NS];
+    f4 rsum[MT];
+  };
+  Slot rg[S];
+
+  auto issue = [&](int64_t b, Slot& r, int slot) __attribute__((always_inline)) {
+    const int64_t g = PERCH ? 0 : b;
+#pragma unroll
+    for (int nt = 0; nt < NS; ++nt) {
+      r.s[nt] = sp[nt][g * kTileN];
+      r.z[nt] = HAS_Z ? zp[nt][g * 2] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) r.rsum[i] = *reinterpret_cast<const f4*>(rp[i] + b * Mr);
+#pragma unroll
+    for (int nt = 0; nt < NS; ++nt) r.w[nt] = wp[nt][b * 64];
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      load_lds16(reinterpret_cast<const uint16_t*>(ap[i] + b * 128),
+                 reinterpret_cast<uint16_t*>(slot_lds(slot) + 8 * (NA * wave + i) * 128));
+  };
+
+  f4 tot[MT][NS];
+  f4 rsacc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    rsacc[i] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < NS; ++nt) tot[i][nt] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto compute = [&](const Slot& r, int slot) __attribute__((always_inline)) {
+    const uint8_t* base = slot_lds(slot);
+    // A: row 16 i + c of the tile, bytes 32 quad .. + 31 (chunks 2 quad, 2 quad + 1)
+    v8i a[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int row = 16 * i + c;
+      const uint8_t* rowp = base + row * 128;
+      const u4 lo = *reinterpret_cast<const u4*>(rowp + 16 * ((2 * quad) ^ swz8(row)));
+      const u4 hi = *reinterpret_cast<const u4*>(rowp + 16 * ((2 * quad + 1) ^ swz8(row)));
+      a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int nt = 0; nt < NS; ++nt) {
+      // B: word j -> (w & 0x0F0F0F0F, (w >> 4) & 0x0F0F0F0F): the bytes of
+      // K-offsets S[0..3] and S[4..7], in operand order
+      v8i bq;
+      const uint32_t w4[4] = {r.w[nt].x, r.w[nt].y, r.w[nt].z, r.w[nt].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bq[2 * j] = (int)(w4[j] & 0x0F0F0F0Fu);
+        bq[2 * j + 1] = (int)((w4[j] >> 4) & 0x0F0F0F0Fu);
+      }
+      const float sf = act_to_f32<BF16>(r.s[nt]);
+      const float z = HAS_Z ? (float)((r.z[nt] >> zshift) & 0xFu) : 8.f;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        if constexpr (PERCH) {
+          tot[i][nt] = mfma_f8(a[i], bq, tot[i][nt]);
+        } else {
+          const f4 p = mfma_f8(a[i], bq, f4{0.f, 0.f, 0.f, 0.f});
+          const float nsz = -sf * z;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            tot[i][nt][q] = __builtin_fmaf(sf, p[q], __builtin_fmaf(nsz, r.rsum[i][q], tot[i][nt][q]));
+        }
+      }
+    }
+    if constexpr (PERCH) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) rsacc[i] += r.rsum[i];
+    }
+  };
+
+  auto iterate = [&](int64_t b, int u) __attribute__((always_inline)) {
+    const int un = (u + S - 1) % S;
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<C::kAfter>();
+    lds_barrier();
+    const int64_t bn = b + S - 1 < nblk ? b + S - 1 : nblk - 1;
+    issue(bn, rg[un], un);
+    compute(rg[u], u);
+  };
+
+#pragma unroll
+  for (int u = 0; u < S - 1; ++u) issue(u < nblk ? u : nblk - 1, rg[u], u);
+  int64_t b = 0;
+  for (; b + S <= nblk; b += S) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) iterate(b + u, u);
+  }
+#pragma unroll
+  for (int u = 0; u < S - 1; ++u)
+    if (b + u < nblk) iterate(b + u, u);
+
+  const float sx = xscale[0];
+#pragma unroll
+  for (int nt = 0; nt < NS; ++nt) {
+    const int64_t t = tw0 + nt;
+    if (t >= T) continue;
+    const int64_t n = t * kTileN + c;
+    if (n >= N) continue;
+    const float bv = bias != nullptr ? act_to_f32<BF16>(bias[n]) : 0.f;
+    float s_ch = 1.f, z_ch = 0.f;
+    if constexpr (PERCH) {
+      s_ch = act_to_f32<BF16>(sp[nt][0]);
+      z_ch = HAS_Z ? (float)((zp[nt][0] >> zshift) & 0xFu) : 8.f;
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t m = m0 + 16 * i + 4 * quad + q;
+        if (m >= M) continue;
+        float v = tot[i][nt][q];
+        if constexpr (PERCH) v = s_ch * (v - z_ch * rsacc[i][q]);
+        y[m * N + n] = f32_to_act<BF16>(sx * v + bv);
+      }
+  }
+}
+
+template <int MT, int NS, int WN, int S, bool PERCH, bool HZ, bool BF16>
+hipError_t run_f8(const Shape& s, int64_t M, const uint8_t* xq, const float* rs, const float* xscale,
+                  const int32_t* tw, const void* ts, const int32_t* tz, const void* bias, void* y, hipStream_t st) {
+  using C = F8Cfg<MT, NS, WN, S>;
+  const int64_t T = s.Np / kTileN;
+  const dim3 grid((unsigned)((T + NS * WN - 1) / (NS * WN)), (unsigned)((M + C::BM - 1) / C::BM));
+  gemm_f8<MT, NS, WN, S, PERCH, HZ, BF16><<<grid, 64 * WN, 0, st>>>(
+      xq, rs, xscale, reinterpret_cast<const u4*>(tw), static_cast<const uint16_t*>(ts),
+      reinterpret_cast<const uint32_t*>(tz), static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), M,
+      (int64_t)f8_rows(M), s.K, s.N, s.G);
+  return hipGetLastError();
+}
+
+template <int MT, int NS, int WN, int S>
+hipError_t f8_flags(const Shape& s, int64_t M, const uint8_t* xq, const float* rs, const float* xscale,
+                    const int32_t* tw, const void* ts, const int32_t* tz, const void* bias, void* y, hipStream_t st) {
+  const bool perch = s.Gp == 1;
+#define W4_F8(P, Z, B) run_f8<MT, NS, WN, S, P, Z, B>(s, M, xq, rs, xscale, tw, ts, tz, bias, y, st)
+  if (s.bf16) {
+    if (perch) return s.has_z ? W4_F8(true, true, true) : W4_F8(true, false, true);
+    return s.has_z ? W4_F8(false, true, true) : W4_F8(false, false, true);
+  }
+  if (perch) return s.has_z ? W4_F8(true, true, false) : W4_F8(true, false, false);
+  return s.has_z ? W4_F8(false, true, false) : W4_F8(false, false, false);
+#undef W4_F8
+}
+
+}  // namespace
+
+size_t f8_rows(int64_t M) { return (size_t)((M + 3) / 4 * 4); }
+
+// Workspace of a W4A8 call: the quantized activations [M][Kp] (256-byte
+// aligned), then the block row sums [Kp / 128][Mr] fp32.
+size_t f8_xq_bytes(const Shape& s, int64_t M) { return ((size_t)M * (size_t)s.Kp + 255) / 256 * 256; }
+size_t f8_workspace_bytes(const Shape& s, int64_t M) {
+  return f8_xq_bytes(s, M) + (size_t)(s.Kp / kTileK) * f8_rows(M) * sizeof(float);
+}
+
+const char* f8_kernel_name(int64_t M) {
+  if (M <= 16) return "w4a8_f8_16x32";
+  if (M <= 128) return "w4a8_f8_64x128";
+  return "w4a8_f8_128x128";
+}
+
+hipError_t launch_f8_quantize(const Shape& s, int64_t M, const void* x, const float* xscale, const int32_t* perm,
+                              uint8_t* xq, float* rs, hipStream_t st) {
+  // s: the unpadded shape (x rows are K long; xq rows are Kp long)
+  const int64_t Mr = (int64_t)f8_rows(M);
+  const int64_t total = Mr * (s.Kp / 8);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  const uint16_t* xx = static_cast<const uint16_t*>(x);
+#define W4_Q(B, P) quant_fp8<B, P><<<(unsigned)blocks, 256, 0, st>>>(xx, xscale, perm, xq, rs, M, Mr, s.K, s.Kp)
+  if (s.bf16) {
+    if (perm) W4_Q(true, true);
+    else W4_Q(true, false);
+  } else {
+    if (perm) W4_Q(false, true);
+    else W4_Q(false, false);
+  }
+#undef W4_Q
+  return hipGetLastError();
+}
+
+hipError_t launch_f8_gemm(const Shape& s, int64_t M, const uint8_t* xq, const float* rs, const float* xscale,
+                          const int32_t* tiled_w, const void* tiled_s, const int32_t* tiled_z, const void* bias,
+                          void* y, hipStream_t st) {
+  if (M <= 16) return f8_flags<1, 1, 2, 4>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+  if (M <= 128) return f8_flags<4, 2, 4, 3>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+  return f8_flags<8, 2, 4, 2>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+}
+
+}  // namespace w4

@@ -94,6 +94,17 @@ int64_t big_tile_cols();
 hipError_t launch_big(const Shape& s, int64_t M, const uint16_t* x, const int32_t* tiled_w, const void* tiled_s,
                       const int32_t* tiled_z, const void* bias, void* y, hipStream_t st);
 
+// ---- INT4 weights x FP8 activations (w4_fp8.hip); the GEMM takes the padded shape ----
+size_t f8_rows(int64_t M);  // rows of the row-sum array (M rounded up to 4)
+size_t f8_xq_bytes(const Shape& s, int64_t M);
+size_t f8_workspace_bytes(const Shape& s, int64_t M);
+const char* f8_kernel_name(int64_t M);
+hipError_t launch_f8_quantize(const Shape& s_unpadded, int64_t M, const void* x, const float* xscale,
+                              const int32_t* perm, uint8_t* xq, float* rs, hipStream_t st);
+hipError_t launch_f8_gemm(const Shape& s, int64_t M, const uint8_t* xq, const float* rs, const float* xscale,
+                          const int32_t* tiled_w, const void* tiled_s, const int32_t* tiled_z, const void* bias,
+                          void* y, hipStream_t st);
+
 // ---- grouped (mixture-of-experts) GEMM (w4_moe.hip) ----
 GemmPlan plan_moe(const Shape& s, int64_t max_rows, int experts);
 hipError_t launch_moe(const Shape& s, int experts, int64_t total_rows, int64_t max_rows, const void* x,

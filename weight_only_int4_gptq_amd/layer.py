@@ -137,6 +137,39 @@ class W4A16Linear:
             cache[key] = ws
         return ws
 
+    def apply_fp8(self, x: torch.Tensor, x_scale: torch.Tensor, bias=None, out=None, stream=None) -> torch.Tensor:
+        """y = s_x x_q W + bias with fp8 (E4M3) activations x_q = e4m3(x / s_x):
+        the W4A8 path (w4a8_linear).  x [..., K] in the activation dtype,
+        x_scale a one-element float32 tensor on the device (the static
+        per-tensor input scale).  Group size 128 or per-channel."""
+        if self.tiled is None:
+            raise RuntimeError("process_weights_after_loading has not run")
+        dt = _TORCH_DTYPE[self.dtype]
+        dev = self.tiled["qweight"].device
+        if x.dtype != dt or x.device != dev or x.shape[-1] != self.K:
+            raise ValueError(f"x must be [..., {self.K}] {dt} on {dev}; got {tuple(x.shape)} {x.dtype} on {x.device}")
+        if x_scale.dtype != torch.float32 or x_scale.device != dev or x_scale.numel() != 1:
+            raise ValueError("x_scale must be a one-element float32 tensor on the layer's device")
+        if bias is not None and (bias.dtype != dt or bias.device != dev or tuple(bias.shape) != (self.N,)
+                                 or not bias.is_contiguous()):
+            raise ValueError(f"bias must be a contiguous [{self.N}] {dt} tensor on {dev}")
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, self.K)
+        if not x2.is_contiguous():
+            x2 = x2.contiguous()
+        M = x2.shape[0]
+        if out is not None and (out.dtype != dt or out.device != dev or tuple(out.shape) != (M, self.N)
+                                or not out.is_contiguous()):
+            raise ValueError(f"out must be a contiguous [{M}, {self.N}] {dt} tensor on {dev}")
+        y = out if out is not None else torch.empty((M, self.N), dtype=dt, device=dev)
+        ws_bytes = A.w4a8_workspace_size(self.layer, M)
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        ws = self._workspace(ws_bytes, st) if ws_bytes else None
+        t = self.tiled
+        A.w4a8_linear(self.layer, M, x2, x_scale, t["qweight"], t["scales"], t["qzeros"], t["perm"], bias, y, ws,
+                      ws_bytes, st)
+        return y.reshape(*lead, self.N)
+
     def dequantize_dense(self, out=None, stream=None) -> torch.Tensor:
         """The dense weight W [K, N] in the activation dtype (for the unfused
         dequantize-then-matmul comparison; the fused apply() never builds it)."""
