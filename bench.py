@@ -1,7 +1,7 @@
 """Benchmark of the W4A16 linear layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config all|decode|tiny|mid|prefill|actorder|moe] [--compare] [--group-size G]
+                    [--config all|decode|tiny|mid|prefill|actorder|w4a8|moe] [--compare] [--group-size G]
 
 A step is one forward pass of the hot path over every (shape, M) case of the
 decode workload (7B-class layers, M = 1, 4, 16): for each case one
@@ -18,7 +18,10 @@ workload (decode, tiny, mid-batch, prefill, act-order), so the metric is
 covered over M = 1..8192: each case is timed alone as the median of five
 replays of a graph of back-to-back launches, and each block reports its
 roofline (HBM-bound cases against 8 TB/s on algorithmic bytes, MFMA-bound
-cases against the dense fp16/bf16 peak on 2 M K N flops).
+cases against the dense fp16/bf16 peak on 2 M K N flops).  A last block,
+"w4a8", runs the decode and prefill layers with FP8-E4M3 activations
+(w4a8_linear: activation quantization plus the int4 x fp8 GEMM, per call),
+its MFMA-bound cases priced against the dense fp8 peak.
 
 Weight buffers are rotated over enough copies that every launch reads its
 weights from HBM (the working set exceeds the 256 MB Infinity Cache).  The
@@ -45,12 +48,16 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A16 GEMM TFLOPS + packed-weight HBM GB/s (% roofline), M=1..8192"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
-RIDGE = MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
+MFMA_F8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 ROTATE_BYTES = 512 << 20       # working set per shape, > 256 MB MALL
 COPY_PROBE_BYTES = 256 << 20   # plain device copy used to calibrate byte counters
 REPLAYS = 5                    # per-case timing: median of this many graph replays
-WORKLOADS = ("decode", "tiny", "mid", "prefill", "actorder")
+WORKLOADS = ("decode", "tiny", "mid", "prefill", "actorder", "w4a8")
 CFG_ID = {"tiny": 1, "decode": 2, "mid": 3, "prefill": 4, "actorder": 5}
+# W4A8-fp8 workload: the decode and prefill layers with FP8-E4M3 activations
+# (static per-tensor scale), quantization included in every call
+W4A8_CFGS = (2, 4)
+W4A8_X_SCALE = 0.01171875
 
 
 def parse():
@@ -111,14 +118,15 @@ def case_bytes(c, M):
     return w, w + s + z + x + y + p
 
 
-def roofline_of(cases):
+def roofline_of(cases, mfma_peak=MFMA_F16_PEAK_TFLOPS):
     """Roofline objects of a set of timed cases, one per bound: a case whose
-    flop per algorithmic byte is below the ridge is HBM-bound, else
-    MFMA-bound.  achieved = algorithmic bytes (flops) of the cases / the sum
-    of their per-launch times."""
+    flop per algorithmic byte is below the ridge (MFMA peak / HBM peak) is
+    HBM-bound, else MFMA-bound.  achieved = algorithmic bytes (flops) of the
+    cases / the sum of their per-launch times."""
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     out = []
     for bound in ("hbm", "mfma"):
-        sel = [p for p in cases if (p["_flops"] / p["_tb"] < RIDGE) == (bound == "hbm")]
+        sel = [p for p in cases if (p["_flops"] / p["_tb"] < ridge) == (bound == "hbm")]
         if not sel:
             continue
         us = sum(p["_us"] for p in sel)
@@ -128,8 +136,8 @@ def roofline_of(cases):
                  "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
         else:
             ach = sum(p["_flops"] for p in sel) / (us * 1e-6) / 1e12
-            r = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+            r = {"bound": "mfma", "achieved": round(ach, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                 "frac": round(ach / mfma_peak, 4), "traffic": None}
         r["kernel"] = sorted({p["kernel"] for p in sel})
         r["cases"] = [f"K={p['K']} N={p['N']} M={p['M']}" for p in sel]
         r["per_launch_bytes_avg"] = round(sum(p["_tb"] for p in sel) / len(sel))
@@ -183,7 +191,8 @@ class Bench:
         import dataclasses
         torch, W = self.torch, self.W
         from synthetic import CONFIGS, make_acts, make_layer_inputs
-        cases = [c for c in CONFIGS if c.cfg_id == CFG_ID[name]]
+        fp8 = name == "w4a8"
+        cases = [c for c in CONFIGS if (c.cfg_id in W4A8_CFGS if fp8 else c.cfg_id == CFG_ID[name])]
         gs = self.args.group_size
         if gs:
             cases = [dataclasses.replace(c, group_size=gs, has_gidx=c.has_gidx and gs != -1) for c in cases]
@@ -213,16 +222,22 @@ class Bench:
             for M in c.Ms:
                 xd = _to_dev(torch, make_acts(c, M))
                 yd = torch.empty((M, c.N), dtype=xd.dtype, device="cuda")
-                ws_b = W.w4_workspace_size(lyr.layer, M)
+                ws_b = W.w4a8_workspace_size(lyr.layer, M) if fp8 else W.w4_workspace_size(lyr.layer, M)
                 ws = torch.zeros((max(ws_b, 1),), dtype=torch.uint8, device="cuda")
-                runs.append(dict(c=c, M=M, lyr=lyr, sets=sets, x=xd, y=yd, ws=ws, ws_b=ws_b, i=0,
-                                 kernel=lyr.kernel_name(M)))
+                runs.append(dict(c=c, M=M, lyr=lyr, sets=sets, x=xd, y=yd, ws=ws, ws_b=ws_b, i=0, fp8=fp8,
+                                 xs=torch.tensor([W4A8_X_SCALE], dtype=torch.float32, device="cuda"),
+                                 kernel=("w4a8_quantize + " + W.w4a8_kernel_name(lyr.layer, M)) if fp8
+                                 else lyr.kernel_name(M)))
         return cases, runs, repack
 
     def launch(self, r):
         # the current stream: the capture stream while a HIP graph is recorded
         t = r["sets"][r["i"] % len(r["sets"])]
         r["i"] += 1
+        if r["fp8"]:
+            self.W.w4a8_linear(r["lyr"].layer, r["M"], r["x"], r["xs"], t["qweight"], t["scales"], t["qzeros"],
+                               t["perm"], None, r["y"], r["ws"], r["ws_b"], self.torch.cuda.current_stream())
+            return
         self.W.w4a16_linear(r["lyr"].layer, r["M"], r["x"], t["qweight"], t["scales"], t["qzeros"], t["perm"], None,
                             r["y"], r["ws"] if r["ws_b"] else None, r["ws_b"], self.torch.cuda.current_stream())
 
@@ -250,7 +265,8 @@ class Bench:
                             total_GBps=round(tb / (us * 1e-6) / 1e9, 1),
                             TFLOPS=round(flops / (us * 1e-6) / 1e12, 2),
                             pct_hbm=round(100 * tb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
-                            pct_mfma=round(100 * flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 1),
+                            pct_mfma=round(100 * flops / (us * 1e-6) / 1e12
+                                           / (MFMA_F8_PEAK_TFLOPS if r["fp8"] else MFMA_F16_PEAK_TFLOPS), 1),
                             _wb=wb, _tb=tb, _flops=flops, _us=us))
         return out
 
@@ -259,7 +275,8 @@ class Bench:
         sum_us = sum(p["_us"] for p in per_case)
         wb = sum(p["_wb"] for p in per_case)
         fl = sum(p["_flops"] for p in per_case)
-        roof = roofline_of(per_case)
+        fp8 = name == "w4a8"
+        roof = roofline_of(per_case, MFMA_F8_PEAK_TFLOPS if fp8 else MFMA_F16_PEAK_TFLOPS)
         blk = {
             "workload": f"{name}: " + ", ".join(f"(K={c.K},N={c.N})" for c in cases)
                         + f" x M in {list(c0.Ms)}; {c0.fmt.upper()} "
@@ -267,6 +284,7 @@ class Bench:
                         + (" zeros" if c0.has_zeros else " symmetric") + (" act-order" if c0.has_gidx else "")
                         + ("" if len({c.group_size for c in cases}) == 1 else " (+ per-channel variant)"),
             "act_dtype": c0.dtype,
+            "compute_dtype": "fp8 e4m3 x int4 (static per-tensor activation scale)" if fp8 else c0.dtype,
             "cases": len(per_case),
             # each case once, back to back: packed-weight GB/s and flops of the set
             "weight_GBps": round(wb / (sum_us * 1e-6) / 1e9, 1),

@@ -200,3 +200,35 @@ def test_noalloc_linear_rejects_before_any_launch(W):
     for K, N in ((8192, 10240), (8192, 8192), (28672, 8192)):
         for M in (32, 64, 128, 256):
             assert W.w4_workspace_size(W.make_layer(K, N, 128, False, False, "bf16"), M) <= W.w4_noalloc_scratch_bytes()
+
+
+def test_w4a8_rejects_before_any_launch(W):
+    lib = W.lib()
+    # group sizes other than 128 and per-channel are not W4A8 layers
+    for gs in (32, 64):
+        L = W.make_layer(512, 256, gs, True, False, "fp16")
+        assert W.w4a8_kernel_name(L, 4) == "invalid"
+        assert lib.w4a8_linear(ctypes.byref(L), 4, 16, 16, 16, 16, 16, None, None, 16, 16, 1 << 20, None) == \
+            W.W4_ERR_UNSUPPORTED
+    L = W.make_layer(512, 256, 128, True, False, "fp16")
+    # workspace: quantized activations [M][Kp] (256-byte aligned), then the
+    # block sums [Kp/128][M rounded up to 4] fp32
+    assert W.w4a8_workspace_size(L, 5) == 5 * 512 + (512 // 128) * 8 * 4          # 2560 is 256-aligned
+    assert W.w4a8_workspace_size(L, 3) == 1536 + 4 * 4 * 4
+    assert W.w4a8_workspace_size(L, 1) == 512 + 4 * 4 * 4
+    assert W.w4a8_workspace_size(W.make_layer(256, 40, 128, True, False, "fp16"), 1) == 256 + 2 * 4 * 4
+    assert W.w4a8_workspace_size(W.make_layer(224, 40, -1, False, False, "bf16"), 3) == 3 * 256 + 2 * 4 * 4
+    assert W.w4a8_workspace_size(W.make_layer(128, 40, -1, False, False, "bf16"), 1) == 256 + 1 * 4 * 4
+
+    def lin(M, x=16, xs=16, ws=16, wsb=1 << 20):
+        return lib.w4a8_linear(ctypes.byref(L), M, x, xs, 16, 16, 16, None, None, 16, ws, wsb, None)
+
+    assert lin(0) == W.W4_OK
+    assert lin(4, x=None) == W.W4_ERR_INVALID_ARGUMENT
+    assert lin(4, xs=None) == W.W4_ERR_INVALID_ARGUMENT
+    assert lin(4, xs=18) == W.W4_ERR_INVALID_ARGUMENT      # fp32 scale, 4-byte aligned
+    assert lin(4, wsb=W.w4a8_workspace_size(L, 4) - 1) == W.W4_ERR_WORKSPACE
+    q = lib.w4a8_quantize
+    assert q(ctypes.byref(L), 4, 16, 16, 16, 16, 16, None) == W.W4_ERR_INVALID_ARGUMENT   # perm without act-order
+    assert q(ctypes.byref(L), 4, 16, 16, None, 12, 16, None) == W.W4_ERR_INVALID_ARGUMENT  # xq 8-byte aligned
+    assert q(ctypes.byref(L), 0, 16, 16, None, 16, 16, None) == W.W4_OK

@@ -343,9 +343,9 @@ size_t f8_workspace_bytes(const Shape& s, int64_t M) {
 }
 
 const char* f8_kernel_name(int64_t M) {
-  if (M <= 16) return "w4a8_f8_16x32";
+  if (M <= 16) return "w4a8_f8_16x16";
   if (M <= 128) return "w4a8_f8_64x128";
-  return "w4a8_f8_128x128";
+  return "w4a8_f8_64x256";
 }
 
 hipError_t launch_f8_quantize(const Shape& s, int64_t M, const void* x, const float* xscale, const int32_t* perm,
@@ -371,9 +371,12 @@ hipError_t launch_f8_quantize(const Shape& s, int64_t M, const void* x, const fl
 hipError_t launch_f8_gemm(const Shape& s, int64_t M, const uint8_t* xq, const float* rs, const float* xscale,
                           const int32_t* tiled_w, const void* tiled_s, const int32_t* tiled_z, const void* bias,
                           void* y, hipStream_t st) {
-  if (M <= 16) return f8_flags<1, 1, 2, 4>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+  // one wave per 16 columns for decode rows; 64 x 256 tiles of four waves
+  // (each 64 x 64) for prefill, which measured fastest among the 64- and
+  // 128-row shapes at 2048 and 8192 rows
+  if (M <= 16) return f8_flags<1, 1, 1, 4>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
   if (M <= 128) return f8_flags<4, 2, 4, 3>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
-  return f8_flags<8, 2, 4, 2>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+  return f8_flags<4, 4, 4, 2>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
 }
 
 }  // namespace w4
