@@ -53,6 +53,9 @@ ROTATE_BYTES = 512 << 20       # working set per shape, > 256 MB MALL
 COPY_PROBE_BYTES = 256 << 20   # plain device copy used to calibrate byte counters
 REPLAYS = 5                    # per-case timing: median of this many graph replays
 WORKLOADS = ("decode", "tiny", "mid", "prefill", "actorder", "w4a8")
+FLOOR_WORKLOADS = ("decode", "tiny")  # the HBM-bound ones that --floor covers
+FLOOR_SWEEP_WGS = (256, 512, 1024, 2048, 4096)
+FLOOR_SWEEP_THREADS = (256, 512, 1024)
 CFG_ID = {"tiny": 1, "decode": 2, "mid": 3, "prefill": 4, "actorder": 5}
 # W4A8-fp8 workload: the decode and prefill layers with FP8-E4M3 activations
 # (static per-tensor scale), quantization included in every call
@@ -73,6 +76,9 @@ def parse():
                    help="run the workloads' shapes with this group size instead (0 = their own)")
     p.add_argument("--compare", action="store_true",
                    help="also time the unfused path (dense dequantization kernel, then torch.matmul) per case")
+    p.add_argument("--floor", action="store_true",
+                   help="per HBM-bound case, also time a plain streaming read of the case's algorithmic bytes "
+                        "and an empty kernel, both on the GEMM's own grid (libw4floor)")
     p.add_argument("--eager", action="store_true",
                    help="time direct launches instead of HIP-graph replays (host launch cost included)")
     return p.parse_args()
@@ -299,7 +305,84 @@ class Bench:
     def workload(self, name):
         cases, runs, repack = self.setup(name)
         pc = self.per_case(runs)
-        return cases, runs, pc, self.block(name, cases, runs, pc, repack)
+        blk = self.block(name, cases, runs, pc, repack)
+        if self.args.floor and name in FLOOR_WORKLOADS:
+            blk["floor"] = self.floor(runs, pc)
+        return cases, runs, pc, blk
+
+    def floor(self, runs, per_case):
+        """What a launch on the GEMM's grid can reach at this size: per case,
+        a plain streaming read of the case's algorithmic bytes (rotated over
+        buffers like the weights) and an empty kernel, both launched with the
+        GEMM kernel's grid and workgroup size and timed like the GEMM (median
+        of REPLAYS graph replays, per launch).  The streaming rate is the
+        case's achievable target; gemm_frac_of_target = stream_us / gemm_us."""
+        import ctypes
+        torch, W = self.torch, self.W
+        F = ctypes.CDLL(os.path.join(ROOT, "weight_only_int4_gptq_amd", "libw4floor.so"))
+        F.w4floor_stream.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint32),
+                                     ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        F.w4floor_empty.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_uint32, ctypes.c_int,
+                                    ctypes.c_void_p]
+        sink = torch.zeros((1,), dtype=torch.int32, device="cuda")
+        cases = []
+        for tag, (r, p) in enumerate(zip(runs, per_case)):
+            grid, threads = W.w4_launch_dims(r["lyr"].layer, r["M"])
+            g = (ctypes.c_uint32 * 3)(*grid)
+            nbytes = (p["_tb"] + 15) // 16 * 16
+            R = max(2, math.ceil(ROTATE_BYTES / nbytes))
+            bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda") for _ in range(R)]
+
+            def stream(n, bufs=bufs, g=g, threads=threads, nbytes=nbytes, tag=tag):
+                st = torch.cuda.current_stream().cuda_stream
+                for i in range(n):
+                    e = F.w4floor_stream(bufs[i % R].data_ptr(), nbytes, g, threads, sink.data_ptr(), tag % 16, st)
+                    assert e == 0, f"w4floor_stream: hip error {e}"
+
+            def empty(n, g=g, threads=threads, tag=tag):
+                st = torch.cuda.current_stream().cuda_stream
+                for _ in range(n):
+                    e = F.w4floor_empty(g, threads, tag % 16, st)
+                    assert e == 0, f"w4floor_empty: hip error {e}"
+
+            stream(R)
+            empty(1)
+            torch.cuda.synchronize()
+            reps = p["reps"]
+            s_us = self.timed(stream, reps, REPLAYS) * 1e3 / reps
+            e_us = self.timed(empty, reps, REPLAYS) * 1e3 / reps
+            # the same bytes on other grids: the fastest plain streaming read found
+            best = (s_us, list(grid), threads)
+            for wgs in FLOOR_SWEEP_WGS:
+                for th in FLOOR_SWEEP_THREADS:
+                    g2 = (ctypes.c_uint32 * 3)(wgs, 1, 1)
+                    us2 = self.timed(lambda n, g2=g2, th=th: stream(n, g=g2, threads=th), reps, REPLAYS) * 1e3 / reps
+                    if us2 < best[0]:
+                        best = (us2, [wgs, 1, 1], th)
+            cases.append(dict(K=p["K"], N=p["N"], M=p["M"], kernel=p["kernel"], tag=tag % 16, grid=list(grid),
+                              threads=threads, alg_bytes=p["_tb"], gemm_us=p["us"], stream_us=round(s_us, 3),
+                              empty_us=round(e_us, 3),
+                              target_GBps=round(p["_tb"] / (s_us * 1e-6) / 1e9, 1),
+                              target_frac_of_peak=round(p["_tb"] / (s_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                              gemm_frac_of_target=round(s_us / p["_us"], 4),
+                              best_stream_us=round(best[0], 3), best_stream_grid=best[1],
+                              best_stream_threads=best[2],
+                              best_stream_frac_of_peak=round(p["_tb"] / (best[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                              gemm_frac_of_best_stream=round(best[0] / p["_us"], 4)))
+            del bufs
+        tot_b = sum(c["alg_bytes"] for c in cases)
+        tot_s = sum(c["stream_us"] for c in cases)
+        tot_best = sum(c["best_stream_us"] for c in cases)
+        tot_g = sum(c["gemm_us"] for c in cases)
+        return {"what": "streaming read of each case's algorithmic bytes, and an empty kernel, on the GEMM's grid; "
+                        "best_stream: the fastest streaming read of the same bytes over grids of "
+                        f"{list(FLOOR_SWEEP_WGS)} workgroups x {list(FLOOR_SWEEP_THREADS)} threads and the GEMM's",
+                "target_GBps": round(tot_b / (tot_s * 1e-6) / 1e9, 1),
+                "best_stream_GBps": round(tot_b / (tot_best * 1e-6) / 1e9, 1),
+                "gemm_GBps": round(tot_b / (tot_g * 1e-6) / 1e9, 1),
+                "gemm_frac_of_target": round(tot_s / tot_g, 4),
+                "gemm_frac_of_best_stream": round(tot_best / tot_g, 4),
+                "per_case": cases}
 
     def steps(self, runs):
         """The timed steps of the headline: K passes over every case."""

@@ -100,6 +100,14 @@ w4_status w4_workspace_size(const w4_layer* layer, int64_t M, size_t* bytes);
  * "invalid" for a bad descriptor.  Static string; host only. */
 const char* w4_kernel_name(const w4_layer* layer, int64_t M);
 
+/* Launch dimensions of the GEMM kernel that w4a16_linear runs for M >= 1
+ * rows (the kernel w4_kernel_name names): grid[0..2] workgroups along x, y,
+ * z and *threads work-items per workgroup.  The act-order gather, K-tail
+ * padding and split-K reduction launches are not included.  For sizing
+ * comparison launches (a streaming-read or empty kernel on the same grid).
+ * Host only; W4_ERR_INVALID_ARGUMENT for M < 1 or NULL outputs. */
+w4_status w4_launch_dims(const w4_layer* layer, int64_t M, uint32_t grid[3], uint32_t* threads);
+
 /* Static description of a status code. */
 const char* w4_status_str(w4_status s);
 

@@ -108,6 +108,43 @@ def test_workspace_and_kernel_name(W):
     assert W.w4_status_str(99) == "unknown status"
 
 
+def test_launch_dims_follow_the_kernel_choice(W):
+    # skinny, activations in LDS: one workgroup of 8 waves per 16-column strip
+    L = W.make_layer(4096, 12288)
+    assert W.w4_kernel_name(L, 1) == "w4_skinny_lds_k8"
+    assert W.w4_launch_dims(L, 1) == ((768, 1, 1), 512)
+    # skinny, 16 waves, one strip per workgroup
+    L = W.make_layer(4096, 4096)
+    assert W.w4_kernel_name(L, 16) == "w4_skinny_k16"
+    assert W.w4_launch_dims(L, 16) == ((256, 1, 1), 1024)
+    # large M: one 1-D grid of 128 x 256 tiles of four waves
+    L = W.make_layer(8192, 8192)
+    assert W.w4_kernel_name(L, 2048) == "w4_big_128x256"
+    assert W.w4_launch_dims(L, 2048) == ((16 * 32, 1, 1), 256)
+    # split-K wide tiles: the K ranges along z
+    name = W.w4_kernel_name(L, 64)
+    (gx, gy, gz), t = W.w4_launch_dims(L, 64)
+    assert name.endswith("_splitk") and gz > 1 and t % 64 == 0
+    with pytest.raises(W.W4Error):
+        W.w4_launch_dims(L, 0)
+
+
+def test_floor_library_exports_its_kernels():
+    from weight_only_int4_gptq_amd import build
+    if not os.path.exists(build.FLOOR_LIB):
+        build.build()
+    F = ctypes.CDLL(build.FLOOR_LIB)
+    assert hasattr(F, "w4floor_stream") and hasattr(F, "w4floor_empty")
+    # bad sizes and grids are refused on the host (no GPU call is made)
+    F.w4floor_stream.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint32),
+                                 ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    F.w4floor_empty.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p]
+    g = (ctypes.c_uint32 * 3)(4, 1, 1)
+    assert F.w4floor_stream(16, 24, g, 256, 16, 0, None) != 0        # bytes not a multiple of 16
+    assert F.w4floor_stream(16, 32, g, 100, 16, 0, None) != 0        # workgroup not whole waves
+    assert F.w4floor_empty((ctypes.c_uint32 * 3)(0, 1, 1), 256, 0, None) != 0
+
+
 def _lin(W, L, M, x=16, qw=16, sc=16, qz=16, perm=None, bias=None, y=16, ws=None, ws_bytes=0):
     return W.lib().w4a16_linear(ctypes.byref(L), M, x, qw, sc, qz, perm, bias, y, ws, ws_bytes, None)
 

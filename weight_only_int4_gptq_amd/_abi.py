@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
             "w4_sizes": ([P(w4_layer), P(w4_sizes_t)], ctypes.c_int),
             "w4_workspace_size": ([P(w4_layer), I64, P(SZ)], ctypes.c_int),
             "w4_kernel_name": ([P(w4_layer), I64], ctypes.c_char_p),
+            "w4_launch_dims": ([P(w4_layer), I64, P(ctypes.c_uint32), P(ctypes.c_uint32)], ctypes.c_int),
             "w4_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "w4_repack_awq": ([P(w4_layer), VP, VP, VP, VP, VP], ctypes.c_int),
             "w4_repack_gptq": ([P(w4_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP], ctypes.c_int),
@@ -128,6 +129,14 @@ def w4_workspace_size(layer: w4_layer, M: int) -> int:
 
 def w4_kernel_name(layer: w4_layer, M: int) -> str:
     return lib().w4_kernel_name(ctypes.byref(layer), int(M)).decode()
+
+
+def w4_launch_dims(layer: w4_layer, M: int):
+    """((gx, gy, gz), threads) of the GEMM kernel w4a16_linear runs for M rows."""
+    g = (ctypes.c_uint32 * 3)()
+    t = ctypes.c_uint32(0)
+    _raise("w4_launch_dims", lib().w4_launch_dims(ctypes.byref(layer), int(M), g, ctypes.byref(t)))
+    return (int(g[0]), int(g[1]), int(g[2])), int(t.value)
 
 
 def w4_repack_awq(layer, awq_qweight, awq_qzeros, std_qweight, std_qzeros, stream=None) -> None:

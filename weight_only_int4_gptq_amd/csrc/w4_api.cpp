@@ -108,6 +108,18 @@ const char* w4_kernel_name(const w4_layer* L, int64_t M) {
   return w4::plan_gemm(w4::padded_k(w4::shape_of(L)), M).name;
 }
 
+w4_status w4_launch_dims(const w4_layer* L, int64_t M, uint32_t grid[3], uint32_t* threads) {
+  const w4_status st = w4_check_layer(L);
+  if (st != W4_OK) return st;
+  if (grid == nullptr || threads == nullptr || M < 1) return W4_ERR_INVALID_ARGUMENT;
+  if (M > kMaxM) return W4_ERR_UNSUPPORTED;
+  unsigned g[3], t = 0;
+  w4::gemm_launch_dims(w4::shape_of(L), M, g, &t);
+  for (int i = 0; i < 3; ++i) grid[i] = g[i];
+  *threads = t;
+  return W4_OK;
+}
+
 const char* w4_status_str(w4_status s) {
   switch (s) {
     case W4_OK: return "ok";

@@ -24,6 +24,7 @@ hipError_t big_z(const Args& a, const uint16_t* x, bool has_z, hipStream_t st) {
 
 int64_t big_tile_rows() { return BigCfg<kBigWM, kBigWN, kBigMT, kBigNT, kBigS>::BM; }
 int64_t big_tile_cols() { return BigCfg<kBigWM, kBigWN, kBigMT, kBigNT, kBigS>::BN; }
+int big_threads() { return 64 * kBigWM * kBigWN; }
 
 hipError_t launch_big(const Shape& s, int64_t M, const uint16_t* x, const int32_t* tiled_w, const void* tiled_s,
                       const int32_t* tiled_z, const void* bias, void* y, hipStream_t st) {

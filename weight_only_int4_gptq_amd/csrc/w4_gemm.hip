@@ -135,6 +135,30 @@ GemmPlan plan_gemm(const Shape& s, int64_t M) {
   return p;
 }
 
+// Grid and workgroup size of the GEMM kernel launch_gemm runs for M rows
+// (the dimensions the run_* launchers compute; s is the unpadded shape).
+void gemm_launch_dims(const Shape& s0, int64_t M, unsigned grid[3], unsigned* threads) {
+  const Shape s = padded_k(s0);
+  const GemmPlan p = plan_gemm(s, M);
+  const int64_t T = s.Np / kTileN;
+  grid[0] = grid[1] = grid[2] = 1;
+  if (p.kind == GemmKind::kSkinny) {
+    grid[0] = (unsigned)(T / p.nb);
+    grid[1] = (unsigned)((M + 16 * p.mt - 1) / (16 * p.mt));
+    *threads = 64u * (unsigned)p.kw;
+  } else if (p.kind == GemmKind::kBig) {
+    grid[0] = (unsigned)(((M + big_tile_rows() - 1) / big_tile_rows()) *
+                         ((s.Np + big_tile_cols() - 1) / big_tile_cols()));
+    *threads = (unsigned)big_threads();
+  } else {
+    const WideChoice& w = kWide[p.wide];
+    grid[0] = (unsigned)((T + w.ns * w.wn - 1) / (w.ns * w.wn));
+    grid[1] = (unsigned)((M + 16 * w.mt - 1) / (16 * w.mt));
+    grid[2] = (unsigned)p.splits;
+    *threads = 64u * (unsigned)w.wn;
+  }
+}
+
 size_t gemm_workspace_bytes(const Shape& s, int64_t M) {
   const GemmPlan p = plan_gemm(padded_k(s), M);
   const size_t part = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)s.N * sizeof(float) : 0;

@@ -84,6 +84,7 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(const Shape& s, int64_t M);
 size_t gemm_workspace_bytes(const Shape& s, int64_t M);
+void gemm_launch_dims(const Shape& s, int64_t M, unsigned grid[3], unsigned* threads);
 hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* tiled_w, const void* tiled_s,
                        const int32_t* tiled_z, const int32_t* perm, const void* bias, void* y, void* ws,
                        hipStream_t st);
@@ -91,6 +92,7 @@ hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* 
 // ---- large-M GEMM on 32x32x16 MFMA tiles, fp16 (w4_big.hip) ----
 int64_t big_tile_rows();
 int64_t big_tile_cols();
+int big_threads();
 hipError_t launch_big(const Shape& s, int64_t M, const uint16_t* x, const int32_t* tiled_w, const void* tiled_s,
                       const int32_t* tiled_z, const void* bias, void* y, hipStream_t st);
 
