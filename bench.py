@@ -55,6 +55,8 @@ REPLAYS = 5                    # per-case timing: median of this many graph repl
 WORKLOADS = ("decode", "tiny", "mid", "prefill", "actorder", "w4a8")
 FLOOR_WORKLOADS = ("decode", "tiny")  # the HBM-bound ones that --floor covers
 FLOOR_SWEEP_WGS = (256, 512, 1024, 2048, 4096)
+FLOOR_TAGS = 15      # empty_kernel<0..14> / stream_read<0..14> name the floor cases
+MARKER_TAG = 15      # empty_kernel<15> on one wave: the --markers case separator
 FLOOR_SWEEP_THREADS = (256, 512, 1024)
 CFG_ID = {"tiny": 1, "decode": 2, "mid": 3, "prefill": 4, "actorder": 5}
 # W4A8-fp8 workload: the decode and prefill layers with FP8-E4M3 activations
@@ -79,23 +81,38 @@ def parse():
     p.add_argument("--floor", action="store_true",
                    help="per HBM-bound case, also time a plain streaming read of the case's algorithmic bytes "
                         "and an empty kernel, both on the GEMM's own grid (libw4floor)")
+    p.add_argument("--markers", action="store_true",
+                   help="launch a one-wave empty kernel (empty_kernel<15>, libw4floor) before each case and after "
+                        "the last, outside every timed region, so that a profiler trace splits into cases")
     p.add_argument("--eager", action="store_true",
                    help="time direct launches instead of HIP-graph replays (host launch cost included)")
     return p.parse_args()
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_decode_hbm_traffic.txt")
-GEMM_SOURCE = os.path.join(ROOT, "weight_only_int4_gptq_amd", "csrc", "w4_gemm.hip")
+CSRC = os.path.join(ROOT, "weight_only_int4_gptq_amd", "csrc")
+
+
+def source_digest():
+    """sha256 over the library's sources (csrc/*.h, *.hip, *.cpp: name and
+    contents, sorted by name): the version that a stored profile was taken of."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(CSRC, "*.hip"))
+                    + glob.glob(os.path.join(CSRC, "*.cpp"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic():
     """HBM bytes per decode GEMM launch from the committed rocprofv3 counter
-    summary, or None when the GEMM source changed since it was measured."""
-    import hashlib
+    summary, or None when the library's sources changed since it was measured."""
     try:
         fields = dict(line.split(": ", 1) for line in open(TRAFFIC_PROFILE).read().splitlines()
                       if line and not line.startswith("#") and ": " in line)
-        cur = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        cur = source_digest()
     except OSError:
         return None
     if fields.get("source_sha256", "").strip() != cur:
@@ -191,6 +208,21 @@ class Bench:
         del g
         return statistics.median(ts)
 
+    def marker(self):
+        """With --markers: one empty one-wave kernel (empty_kernel<15>) on
+        the current stream, a case boundary in a profiler trace."""
+        if not self.args.markers:
+            return
+        import ctypes
+        if not hasattr(self, "_floor_lib"):
+            F = ctypes.CDLL(os.path.join(ROOT, "weight_only_int4_gptq_amd", "libw4floor.so"))
+            F.w4floor_empty.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_uint32, ctypes.c_int,
+                                        ctypes.c_void_p]
+            self._floor_lib = F
+        g = (ctypes.c_uint32 * 3)(1, 1, 1)
+        e = self._floor_lib.w4floor_empty(g, 64, MARKER_TAG, self.torch.cuda.current_stream().cuda_stream)
+        assert e == 0, f"w4floor_empty: hip error {e}"
+
     # ---- workloads ----------------------------------------------------------
     def setup(self, name):
         """Layers (repacked, weight copies for rotation) and per-case buffers."""
@@ -254,6 +286,7 @@ class Bench:
         out = []
         for r in runs:
             c, M = r["c"], r["M"]
+            self.marker()
             for _ in range(3):
                 self.launch(r)
             torch.cuda.synchronize()
@@ -274,6 +307,7 @@ class Bench:
                             pct_mfma=round(100 * flops / (us * 1e-6) / 1e12
                                            / (MFMA_F8_PEAK_TFLOPS if r["fp8"] else MFMA_F16_PEAK_TFLOPS), 1),
                             _wb=wb, _tb=tb, _flops=flops, _us=us))
+        self.marker()
         return out
 
     def block(self, name, cases, runs, per_case, repack):
@@ -336,13 +370,13 @@ class Bench:
             def stream(n, bufs=bufs, g=g, threads=threads, nbytes=nbytes, tag=tag):
                 st = torch.cuda.current_stream().cuda_stream
                 for i in range(n):
-                    e = F.w4floor_stream(bufs[i % R].data_ptr(), nbytes, g, threads, sink.data_ptr(), tag % 16, st)
+                    e = F.w4floor_stream(bufs[i % R].data_ptr(), nbytes, g, threads, sink.data_ptr(), tag % FLOOR_TAGS, st)
                     assert e == 0, f"w4floor_stream: hip error {e}"
 
             def empty(n, g=g, threads=threads, tag=tag):
                 st = torch.cuda.current_stream().cuda_stream
                 for _ in range(n):
-                    e = F.w4floor_empty(g, threads, tag % 16, st)
+                    e = F.w4floor_empty(g, threads, tag % FLOOR_TAGS, st)
                     assert e == 0, f"w4floor_empty: hip error {e}"
 
             stream(R)
@@ -359,7 +393,7 @@ class Bench:
                     us2 = self.timed(lambda n, g2=g2, th=th: stream(n, g=g2, threads=th), reps, REPLAYS) * 1e3 / reps
                     if us2 < best[0]:
                         best = (us2, [wgs, 1, 1], th)
-            cases.append(dict(K=p["K"], N=p["N"], M=p["M"], kernel=p["kernel"], tag=tag % 16, grid=list(grid),
+            cases.append(dict(K=p["K"], N=p["N"], M=p["M"], kernel=p["kernel"], tag=tag % FLOOR_TAGS, grid=list(grid),
                               threads=threads, alg_bytes=p["_tb"], gemm_us=p["us"], stream_us=round(s_us, 3),
                               empty_us=round(e_us, 3),
                               target_GBps=round(p["_tb"] / (s_us * 1e-6) / 1e9, 1),
@@ -529,6 +563,7 @@ def main_moe(args, torch, W):
     wbytes = E * K * N // 2
     per_case = []
     for r in runs:
+        B.marker()
         for _ in range(3):
             launch(r)
         torch.cuda.synchronize()
@@ -540,6 +575,7 @@ def main_moe(args, torch, W):
                              kernel="w4a16_moe_linear", us=round(us, 3),
                              weight_GBps=round(wbytes / (us * 1e-6) / 1e9, 1),
                              TFLOPS=round(fl / (us * 1e-6) / 1e12, 2), _tb=tb, _flops=fl, _us=us))
+    B.marker()
 
     for _ in range(args.warmup):
         for r in runs:
