@@ -205,9 +205,14 @@ __device__ __forceinline__ void block_mac(f4 (&tot)[MT][NB], const u4 (&a)[MT][4
 }
 
 // Activation rows staged in LDS (XL kernels): row r of the workgroup's
-// 16-row tile at xs + r * (K + kXPad); the pad of 8 halves moves consecutive
-// rows to different banks.
-constexpr int kXPad = 8;
+// 16-row tile at xs + r * (K + kXPad).  An A-operand read puts the four
+// 16-byte quads of a row on four consecutive 4-bank groups (16 banks); with
+// K a multiple of 128 the pad of 32 halves starts each row 16 banks after
+// the previous one, so the (at most four) staged rows and their quads fall
+// on 64 distinct banks.  (A pad of 8 halves, one 4-bank group per row,
+// overlapped row r + 1 with quad 1 of row r: 0.6-0.75 bank-conflict cycles
+// per LDS-active cycle at M = 4 in the SQ counters.)
+constexpr int kXPad = 32;
 constexpr int kXlRows = 4;  // at most this many rows are staged (M <= 4)
 
 // Registers of one 128-row block: weights, scales and zeros of NB strips,
@@ -869,7 +874,7 @@ struct Args {
 };
 
 // LDS bytes of a skinny launch: the reduction buffer, plus the staged
-// activation rows (at most 16, row stride K + kXPad halves) when XL.
+// activation rows (at most kXlRows, row stride K + kXPad halves) when XL.
 constexpr size_t kMaxSkinnyLds = 128 * 1024;  // of the CU's 160 KiB
 
 inline size_t skinny_lds_bytes(int mt, int nb, int kw, bool xl, int64_t M, int64_t K) {
