@@ -128,6 +128,7 @@ def test_w4a8_linear_matches_the_oracle(W, v):
 FULL_CASES = [
     # workload shapes with fp8 activations: (label, fmt, K, N, gs, has_z, act, dtype, Ms)
     ("decode-awq-fp16", "awq", 4096, 12288, 128, True, False, "fp16", (1, 16)),
+    ("decode-down-awq-fp16", "awq", 11008, 4096, 128, True, False, "fp16", (1, 4, 16)),
     ("mid-std-bf16-sym", "std", 8192, 8192, 128, False, False, "bf16", (64, 256)),
     ("prefill-awq-fp16", "awq", 8192, 8192, 128, True, False, "fp16", (2048,)),
     ("actorder-fp16", "std", 8192, 8192, 128, True, True, "fp16", (512,)),

@@ -129,6 +129,17 @@ def test_launch_dims_follow_the_kernel_choice(W):
         W.w4_launch_dims(L, 0)
 
 
+def test_w4a8_kernel_choice(W):
+    # decode rows: K split over the waves of a workgroup on narrow layers
+    assert W.w4a8_kernel_name(W.make_layer(4096, 4096), 1) == "w4a8_f8_skinny_k16"
+    assert W.w4a8_kernel_name(W.make_layer(11008, 4096), 16) == "w4a8_f8_skinny_k8"
+    assert W.w4a8_kernel_name(W.make_layer(4096, 12288), 4) == "w4a8_f8_skinny_k8"
+    assert W.w4a8_kernel_name(W.make_layer(4096, 12288), 16) == "w4a8_f8_16x16"
+    assert W.w4a8_kernel_name(W.make_layer(4096, 22016), 1) == "w4a8_f8_16x16"
+    assert W.w4a8_kernel_name(W.make_layer(8192, 8192), 64) == "w4a8_f8_64x128"
+    assert W.w4a8_kernel_name(W.make_layer(8192, 8192), 2048) == "w4a8_f8_64x256"
+
+
 def test_floor_library_exports_its_kernels():
     from weight_only_int4_gptq_amd import build
     if not os.path.exists(build.FLOOR_LIB):

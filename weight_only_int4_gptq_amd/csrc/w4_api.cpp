@@ -306,7 +306,7 @@ w4_status w4a8_linear(const w4_layer* L, int64_t M, const void* x, const float* 
 const char* w4a8_kernel_name(const w4_layer* L, int64_t M) {
   if (w4a8_layer_ok(L) != W4_OK || M < 0 || M > kMaxM) return "invalid";
   if (M == 0) return "none";
-  return w4::f8_kernel_name(M);
+  return w4::f8_kernel_name(w4::padded_k(w4::shape_of(L)), M);
 }
 
 }  // extern "C"

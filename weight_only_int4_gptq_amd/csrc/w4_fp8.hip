@@ -304,6 +304,165 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_f8(const uint8_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode kernel (M <= 16): one 16 x 16 output tile per workgroup, its KW
+// waves splitting K into contiguous block ranges (as the W4A16 skinny
+// kernel).  A wave loads each block's operands straight into registers --
+// the lane's 32 activation bytes (row l % 16, bytes 32 (l / 16) .. + 31 of the
+// block in operand order, 2 KiB per block: L2-resident), its 16 bytes of
+// packed weights, the scale, the zero word and the four row sums -- through
+// a D-deep ring (prefetch index clamped to the wave's last block, so the
+// steady state has no branch), computes one fp8 MFMA per block and folds it
+// into the fp32 total with the group's scale.  The KW partial tiles are
+// summed in LDS in wave order (a fixed order: the result does not depend on
+// timing).  Rows >= M read row M - 1 and are never stored.
+// ---------------------------------------------------------------------------
+template <int KW, int D, bool PERCH, bool HAS_Z, bool BF16>
+__global__ __launch_bounds__(64 * KW) void gemm_f8_skinny(const uint8_t* __restrict__ xq,
+                                                           const float* __restrict__ rs,
+                                                           const float* __restrict__ xscale,
+                                                           const u4* __restrict__ qw, const uint16_t* __restrict__ sc,
+                                                           const uint32_t* __restrict__ zs,
+                                                           const uint16_t* __restrict__ bias,
+                                                           uint16_t* __restrict__ y, int64_t M, int64_t Mr, int64_t K,
+                                                           int64_t N, int G) {
+  static_assert(D >= 2, "ring depth");
+  constexpr int R = PERCH ? 8 : 4;  // partial tile (+ row-sum totals per channel)
+  __shared__ float red[KW * R * 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, quad = lane >> 4;
+  const int64_t t = blockIdx.x;
+  const int nblk = (int)(K / kTileK);
+  const int lo = __builtin_amdgcn_readfirstlane((int)(((int64_t)nblk * wave) / KW));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(((int64_t)nblk * (wave + 1)) / KW));
+  const uint32_t zshift = 4u * (uint32_t)(c & 7);
+
+  const u4* wp = qw + t * nblk * 64 + lane;
+  const uint16_t* sp = sc + t * G * kTileN + c;
+  const uint32_t* zp = HAS_Z ? zs + t * G * 2 + (c >> 3) : nullptr;
+  const int64_t m = c < M ? c : M - 1;
+  const u4* ap = reinterpret_cast<const u4*>(xq + m * K + 32 * quad);
+  const float* rp = rs + (4 * quad < Mr ? 4 * quad : Mr - 4);
+
+  struct Blk {
+    u4 w, a0, a1;
+    f4 rsum;
+    uint32_t z;
+    uint16_t s;
+  };
+  auto load = [&](int b, Blk& r) __attribute__((always_inline)) {
+    const int64_t g = PERCH ? 0 : b;
+    r.w = wp[(int64_t)b * 64];
+    r.s = sp[g * kTileN];
+    r.z = HAS_Z ? zp[g * 2] : 0u;
+    r.rsum = *reinterpret_cast<const f4*>(rp + (int64_t)b * Mr);
+    r.a0 = ap[(int64_t)b * 8];
+    r.a1 = ap[(int64_t)b * 8 + 1];
+  };
+
+  f4 tot = {0.f, 0.f, 0.f, 0.f}, rsacc = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Blk& r) __attribute__((always_inline)) {
+    const v8i a = {(int)r.a0.x, (int)r.a0.y, (int)r.a0.z, (int)r.a0.w,
+                   (int)r.a1.x, (int)r.a1.y, (int)r.a1.z, (int)r.a1.w};
+    const uint32_t w4[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
+    v8i bq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bq[2 * j] = (int)(w4[j] & 0x0F0F0F0Fu);
+      bq[2 * j + 1] = (int)((w4[j] >> 4) & 0x0F0F0F0Fu);
+    }
+    if constexpr (PERCH) {
+      tot = mfma_f8(a, bq, tot);
+      rsacc += r.rsum;
+    } else {
+      const float sf = act_to_f32<BF16>(r.s);
+      const float z = HAS_Z ? (float)((r.z >> zshift) & 0xFu) : 8.f;
+      const f4 p = mfma_f8(a, bq, f4{0.f, 0.f, 0.f, 0.f});
+      const float nsz = -sf * z;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tot[q] = __builtin_fmaf(sf, p[q], __builtin_fmaf(nsz, r.rsum[q], tot[q]));
+    }
+  };
+
+  if (lo < hi) {  // wave-uniform
+    const int last = hi - 1;
+    Blk ring[D];
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u) load(lo + u < last ? lo + u : last, ring[u]);
+    int kb = lo;
+    for (; kb + D <= hi; kb += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        const int nb = kb + u + D - 1;
+        load(nb < last ? nb : last, ring[(u + D - 1) % D]);
+        compute(ring[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u)
+      if (kb + u < hi) compute(ring[u]);
+  }
+
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    red[(wave * R + q) * 64 + lane] = tot[q];
+    if constexpr (PERCH) red[(wave * R + 4 + q) * 64 + lane] = rsacc[q];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int64_t n = t * kTileN + c;
+  if (n >= N) return;  // the padded half of the last strip
+  const float sx = xscale[0];
+  const float bv = bias != nullptr ? act_to_f32<BF16>(bias[n]) : 0.f;
+  float s_ch = 1.f, z_ch = 0.f;
+  if constexpr (PERCH) {
+    s_ch = act_to_f32<BF16>(sp[0]);
+    z_ch = HAS_Z ? (float)((zp[0] >> zshift) & 0xFu) : 8.f;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t mo = 4 * quad + q;
+    if (mo >= M) continue;
+    float v = 0.f, rsa = 0.f;
+#pragma unroll
+    for (int w = 0; w < KW; ++w) {
+      v += red[(w * R + q) * 64 + lane];
+      if constexpr (PERCH) rsa += red[(w * R + 4 + q) * 64 + lane];
+    }
+    if constexpr (PERCH) v = s_ch * (v - z_ch * rsa);
+    y[mo * N + n] = f32_to_act<BF16>(sx * v + bv);
+  }
+}
+
+template <int KW, int D, bool PERCH, bool HZ, bool BF16>
+hipError_t run_f8_skinny(const Shape& s, int64_t M, const uint8_t* xq, const float* rs, const float* xscale,
+                         const int32_t* tw, const void* ts, const int32_t* tz, const void* bias, void* y,
+                         hipStream_t st) {
+  if (M < 1 || M > 16) return hipErrorInvalidValue;
+  const int64_t T = s.Np / kTileN;
+  gemm_f8_skinny<KW, D, PERCH, HZ, BF16><<<(unsigned)T, 64 * KW, 0, st>>>(
+      xq, rs, xscale, reinterpret_cast<const u4*>(tw), static_cast<const uint16_t*>(ts),
+      reinterpret_cast<const uint32_t*>(tz), static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), M,
+      (int64_t)f8_rows(M), s.K, s.N, s.G);
+  return hipGetLastError();
+}
+
+template <int KW, int D>
+hipError_t f8_skinny_flags(const Shape& s, int64_t M, const uint8_t* xq, const float* rs, const float* xscale,
+                           const int32_t* tw, const void* ts, const int32_t* tz, const void* bias, void* y,
+                           hipStream_t st) {
+  const bool perch = s.Gp == 1;
+#define W4_F8S(P, Z, B) run_f8_skinny<KW, D, P, Z, B>(s, M, xq, rs, xscale, tw, ts, tz, bias, y, st)
+  if (s.bf16) {
+    if (perch) return s.has_z ? W4_F8S(true, true, true) : W4_F8S(true, false, true);
+    return s.has_z ? W4_F8S(false, true, true) : W4_F8S(false, false, true);
+  }
+  if (perch) return s.has_z ? W4_F8S(true, true, false) : W4_F8S(true, false, false);
+  return s.has_z ? W4_F8S(false, true, false) : W4_F8S(false, false, false);
+#undef W4_F8S
+}
+
 template <int MT, int NS, int WN, int S, bool PERCH, bool HZ, bool BF16>
 hipError_t run_f8(const Shape& s, int64_t M, const uint8_t* xq, const float* rs, const float* xscale,
                   const int32_t* tw, const void* ts, const int32_t* tz, const void* bias, void* y, hipStream_t st) {
@@ -342,7 +501,10 @@ size_t f8_workspace_bytes(const Shape& s, int64_t M) {
   return f8_xq_bytes(s, M) + (size_t)(s.Kp / kTileK) * f8_rows(M) * sizeof(float);
 }
 
-const char* f8_kernel_name(int64_t M) {
+const char* f8_kernel_name(const Shape& s, int64_t M) {
+  const int64_t T = s.Np / kTileN;
+  if (M <= 16 && T <= 256) return M <= 4 ? "w4a8_f8_skinny_k16" : "w4a8_f8_skinny_k8";
+  if (M <= 4 && T <= 1024) return "w4a8_f8_skinny_k8";
   if (M <= 16) return "w4a8_f8_16x16";
   if (M <= 128) return "w4a8_f8_64x128";
   return "w4a8_f8_64x256";
@@ -371,9 +533,19 @@ hipError_t launch_f8_quantize(const Shape& s, int64_t M, const void* x, const fl
 hipError_t launch_f8_gemm(const Shape& s, int64_t M, const uint8_t* xq, const float* rs, const float* xscale,
                           const int32_t* tiled_w, const void* tiled_s, const int32_t* tiled_z, const void* bias,
                           void* y, hipStream_t st) {
-  // one wave per 16 columns for decode rows; 64 x 256 tiles of four waves
-  // (each 64 x 64) for prefill, which measured fastest among the 64- and
-  // 128-row shapes at 2048 and 8192 rows
+  // Decode rows (M <= 16), from timing sweeps of the 7B-class decode layers:
+  // up to 256 strips (N <= 4096), the K-split kernel (16 waves, 3-deep ring
+  // up to 4 rows; 8 waves, 6-deep above); up to 1024 strips, the K-split
+  // kernel with 8 waves at M <= 4; otherwise one wave walking all of K per
+  // 16 columns.  Prefill: 64 x 256 tiles of four waves (each 64 x 64), which
+  // measured fastest among the 64- and 128-row shapes at 2048 and 8192 rows.
+  const int64_t T = s.Np / kTileN;
+  if (M <= 16 && T <= 256) {
+    if (M <= 4) return f8_skinny_flags<16, 3>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+    return f8_skinny_flags<8, 6>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+  }
+  if (M <= 4 && T <= 1024)
+    return f8_skinny_flags<8, 2>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
   if (M <= 16) return f8_flags<1, 1, 1, 4>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
   if (M <= 128) return f8_flags<4, 2, 4, 3>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
   return f8_flags<4, 4, 4, 2>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);

@@ -100,7 +100,7 @@ hipError_t launch_big(const Shape& s, int64_t M, const uint16_t* x, const int32_
 size_t f8_rows(int64_t M);  // rows of the row-sum array (M rounded up to 4)
 size_t f8_xq_bytes(const Shape& s, int64_t M);
 size_t f8_workspace_bytes(const Shape& s, int64_t M);
-const char* f8_kernel_name(int64_t M);
+const char* f8_kernel_name(const Shape& s, int64_t M);  // s: the padded shape
 hipError_t launch_f8_quantize(const Shape& s_unpadded, int64_t M, const void* x, const float* xscale,
                               const int32_t* perm, uint8_t* xq, float* rs, hipStream_t st);
 hipError_t launch_f8_gemm(const Shape& s, int64_t M, const uint8_t* xq, const float* rs, const float* xscale,
