@@ -90,9 +90,14 @@ w4_status w4_check_layer(const w4_layer* layer);
 /* Fill *out with the byte sizes of the layer's buffers.  Host only. */
 w4_status w4_sizes(const w4_layer* layer, w4_sizes_t* out);
 
-/* Bytes of scratch device memory w4a16_linear needs for M rows (0 when the
- * chosen kernel needs none: K % 128 == 0 and M <= 16 without act-order,
- * M > 256, or layers with N > 16384 and no act-order).  Host only. */
+/* Bytes of scratch device memory w4a16_linear needs for M rows, in three
+ * 256-byte-aligned parts: the activations gathered through perm (act-order,
+ * M K 2 bytes) or zero-padded to whole 128-row blocks (K tails); split-K
+ * fp32 partials [splits][M][N] (16 < M <= 256 on layers with N <= 16384);
+ * and, for bf16 from M = 256 (M = 64 on layers with K >= 16384 or
+ * N > 16384), fp32 row sums of x per scale period [Kp / L][M] (L = the group
+ * size, at most 128).  0 when none applies (fp16 with K % 128 == 0 and no
+ * act-order outside the split-K range, for instance).  Host only. */
 w4_status w4_workspace_size(const w4_layer* layer, int64_t M, size_t* bytes);
 
 /* Name of the kernel w4a16_linear launches for M rows (the analogue of the

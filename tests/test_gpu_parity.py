@@ -479,6 +479,11 @@ WIDE_VARIANTS = [
     ("std-fp16-ch-z", "std", -1, True, False, "fp16", 1152),
     ("std-fp16-g128-z-act", "std", 128, True, True, "fp16", 1152),
     ("std-fp16-g64-sym", "std", 64, False, False, "fp16", 1152),
+    # bf16 at M >= 256 (and M = 64 on wide layers) reads the row sums of a
+    # pre-pass: four sums per block at g = 32, and act-order (sums of the
+    # gathered columns)
+    ("std-bf16-g32-z", "std", 32, True, False, "bf16", 1152),
+    ("std-bf16-g128-z-act", "std", 128, True, True, "bf16", 1152),
     # K tails: nine blocks after padding, the last one partly padding
     ("awq-fp16-g32-z-k1120", "awq", 32, True, False, "fp16", 1120),
     ("std-bf16-ch-sym-k1056", "std", -1, False, False, "bf16", 1056),

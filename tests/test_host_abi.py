@@ -203,13 +203,21 @@ def test_split_k_workspace_is_sized_and_checked(W):
     assert W.w4_workspace_size(L, 32) == 4 * 32 * 8192 * 4
     assert W.w4_workspace_size(L, 64) == 4 * 64 * 8192 * 4
     assert W.w4_workspace_size(L, 128) == 4 * 128 * 8192 * 4
-    assert W.w4_workspace_size(L, 1) == 0 and W.w4_workspace_size(L, 2048) == 0
+    assert W.w4_workspace_size(L, 1) == 0
+    # bf16 from M = 256 (and M = 64 on long or wide layers): the row sums of x
+    # per 128-row block follow, [K / 128][M] fp32
+    assert W.w4_workspace_size(L, 256) == 4 * 256 * 8192 * 4 + 64 * 256 * 4
+    assert W.w4_workspace_size(L, 2048) == 64 * 2048 * 4
     # a longer K splits eight ways (four at M = 256)
     L2 = W.make_layer(28672, 8192, 128, False, False, "bf16")
     assert W.w4_workspace_size(L2, 32) == 8 * 32 * 8192 * 4
-    assert W.w4_workspace_size(L2, 256) == 4 * 256 * 8192 * 4
-    # N = 57344 has workgroups enough: no split
-    assert W.w4_workspace_size(W.make_layer(8192, 57344, 128, False, False, "bf16"), 128) == 0
+    assert W.w4_workspace_size(L2, 64) == 8 * 64 * 8192 * 4 + 224 * 64 * 4
+    assert W.w4_workspace_size(L2, 256) == 4 * 256 * 8192 * 4 + 224 * 256 * 4
+    # N = 57344 has workgroups enough: no split, only the row sums
+    assert W.w4_workspace_size(W.make_layer(8192, 57344, 128, False, False, "bf16"), 128) == 64 * 128 * 4
+    # g = 32: four sums per block; fp16 layers need none
+    assert W.w4_workspace_size(W.make_layer(8192, 57344, 32, False, False, "bf16"), 128) == 256 * 128 * 4
+    assert W.w4_workspace_size(W.make_layer(8192, 57344, 128, False, False, "fp16"), 128) == 0
     # act-order: the gathered activations (256-byte aligned) come first
     La = W.make_layer(8192, 8192, 128, True, True, "fp16")
     assert W.w4_workspace_size(La, 64) == 64 * 8192 * 2 + 4 * 64 * 8192 * 4

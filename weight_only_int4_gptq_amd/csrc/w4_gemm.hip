@@ -16,6 +16,20 @@ inline size_t front_bytes(const Shape& s, const GemmPlan& p, int64_t M) {
   return (b + 255) / 256 * 256;
 }
 
+// Workspace layout: front bytes (gathered or padded activations), split-K
+// partials [splits][M][N] fp32, row sums [Kp / L][M] fp32 (bf16 pre-pass),
+// each part 256-byte aligned.
+size_t partial_bytes(const Shape& s, const GemmPlan& p, int64_t M) {
+  const size_t b = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)s.N * sizeof(float) : 0;
+  return (b + 255) / 256 * 256;
+}
+
+size_t rowsum_bytes(const Shape& sp, const GemmPlan& p, int64_t M) {
+  if (!p.rsin) return 0;
+  const size_t periods = (size_t)(sp.Kp / kTileK) * (size_t)(sp.gs == 32 ? 4 : (sp.gs == 64 ? 2 : 1));
+  return (periods * (size_t)M * sizeof(float) + 255) / 256 * 256;
+}
+
 // Act-order first gathers the columns of x into the workspace (front bytes
 // of the workspace in use by the caller: `front`).
 hipError_t launch_wide(const Shape& s, const GemmPlan& p, const Args& a0, void* ws, size_t front, hipStream_t st) {
@@ -29,6 +43,7 @@ hipError_t launch_wide(const Shape& s, const GemmPlan& p, const Args& a0, void* 
   }
   a.splits = p.splits;
   a.part = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + front) : nullptr;
+  a.rsum = p.rsin ? reinterpret_cast<float*>(static_cast<char*>(ws) + front + partial_bytes(s, p, a.M)) : nullptr;
   return wide_dispatch<false>(p.wide, s, a, x, st);
 }
 
@@ -52,7 +67,25 @@ hipError_t pick_flags(const Shape& s, const Args& a, hipStream_t st) {
 
 }  // namespace
 
+namespace {
+GemmPlan plan_tiles(const Shape& s, int64_t M);
+}  // namespace
+
 GemmPlan plan_gemm(const Shape& s, int64_t M) {
+  GemmPlan p = plan_tiles(s, M);
+  // bf16 wide kernels take the zero-point row sums from a pre-pass
+  // (row_sums_bf16) instead of a ones-operand MFMA per row tile and step
+  // where that measured faster: M >= 256, or M >= 64 on long (K >= 16384)
+  // or wide (> 1024 strips) layers (5-13% there; the extra launch cost more
+  // than it saved below that, e.g. 45.6 -> 46.9 us at 8192 x 10240, M = 128)
+  const int64_t T = s.Np / kTileN;
+  if (s.bf16 && p.kind == GemmKind::kWide && (M >= 256 || (M >= 64 && (s.K >= 16384 || T > 1024))))
+    p.rsin = true;
+  return p;
+}
+
+namespace {
+GemmPlan plan_tiles(const Shape& s, int64_t M) {
   // (mt, nb, kw, xl): 16-row tiles per wave, strips per workgroup, waves per
   // workgroup (splitting K), activations staged in LDS; the ring depth
   // follows from them (skinny_depth).  Chosen from timing sweeps of the
@@ -135,6 +168,8 @@ GemmPlan plan_gemm(const Shape& s, int64_t M) {
   return p;
 }
 
+}  // namespace
+
 // Grid and workgroup size of the GEMM kernel launch_gemm runs for M rows
 // (the dimensions the run_* launchers compute; s is the unpadded shape).
 void gemm_launch_dims(const Shape& s0, int64_t M, unsigned grid[3], unsigned* threads) {
@@ -160,9 +195,9 @@ void gemm_launch_dims(const Shape& s0, int64_t M, unsigned grid[3], unsigned* th
 }
 
 size_t gemm_workspace_bytes(const Shape& s, int64_t M) {
-  const GemmPlan p = plan_gemm(padded_k(s), M);
-  const size_t part = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)s.N * sizeof(float) : 0;
-  return front_bytes(s, p, M) + part;
+  const Shape sp = padded_k(s);
+  const GemmPlan p = plan_gemm(sp, M);
+  return front_bytes(s, p, M) + partial_bytes(s, p, M) + rowsum_bytes(sp, p, M);
 }
 
 hipError_t launch_gemm(const Shape& s0, int64_t M, const void* x, const int32_t* tiled_w, const void* tiled_s,
@@ -183,6 +218,7 @@ hipError_t launch_gemm(const Shape& s0, int64_t M, const void* x, const int32_t*
   a.offs = nullptr;
   a.groups = 0;
   a.max_rows = M;
+  a.rsum = nullptr;
   a.M = M;
   a.K = s.K;
   a.N = s.N;

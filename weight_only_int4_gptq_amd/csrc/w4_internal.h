@@ -80,6 +80,7 @@ struct GemmPlan {
   const char* name;
   int wide = 0;    // wide tile configuration (index into the kernel's table)
   int splits = 1;  // wide kernel: K ranges reduced by a second kernel (1 = none)
+  bool rsin = false;  // bf16 wide kernel: row sums from a pre-pass instead of ones-operand MFMAs
 };
 
 GemmPlan plan_gemm(const Shape& s, int64_t M);

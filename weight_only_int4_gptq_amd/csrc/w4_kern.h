@@ -480,6 +480,11 @@ __device__ __forceinline__ void load_lds16(const uint16_t* src, uint16_t* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
 }
 
+// 4 bytes per lane: lane l's word lands at dst + l (dst is wave-uniform).
+__device__ __forceinline__ void load_lds4(const float* src, float* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
+}
+
 // Workgroup barrier for the pipeline.  __syncthreads() would add a release
 // fence, which waits for every outstanding direct-to-LDS load (they count as
 // LDS writes) and so drains the whole pipeline at every block.  Here each
@@ -503,18 +508,30 @@ struct WideCfg {
   static_assert(S >= 2 && kAfter < 64, "pipeline depth");
 };
 
-template <int MT, int NS, int WN, int S, int GM, bool BF16, bool HAS_Z, bool GROUPED>
+// RSIN (bf16 only): the zero-point term's row sums come from rsum[pd][m]
+// (fp32 sums of x over scale period pd, row_sums_bf16) instead of a ones-operand
+// MFMA per row tile and step: each wave copies the tile's sums of block b into
+// its own LDS area with direct-to-LDS loads in the same pipeline slot.
+template <int MT, int NS, int WN, int S, int GM, bool BF16, bool HAS_Z, bool GROUPED, bool RSIN = false>
 __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restrict__ x,
                                                           const u4* __restrict__ qw,
                                                           const uint16_t* __restrict__ sc,
                                                           const uint32_t* __restrict__ zs,
                                                           const uint16_t* __restrict__ bias,
                                                           uint16_t* __restrict__ y, float* __restrict__ part,
-                                                          const int32_t* __restrict__ offs, int64_t M,
+                                                          const int32_t* __restrict__ offs,
+                                                          const float* __restrict__ rsum, int64_t M,
                                                           int64_t K, int64_t N, int G) {
   using C = WideCfg<MT, NS, WN, S>;
   constexpr int NP = Groups<GM>::kPeriods, SP = Groups<GM>::kSteps;
   constexpr int NA = C::NA;
+  static_assert(!RSIN || (BF16 && !GROUPED), "row sums from memory: plain bf16 launches");
+  // row-sum copies: per wave and period RW floats (the tile's BM rows, at
+  // least one 64-lane load), NR direct-to-LDS loads of 4 bytes per block
+  constexpr int RW = C::BM < 64 ? 64 : C::BM;
+  constexpr int NR = RSIN ? NP * (RW / 64) : 0;
+  constexpr int kAfter = (S - 2) * (NS + NA + NR);
+  static_assert(kAfter < 64, "vmcnt is six bits");
   // One LDS array per pipeline slot (BM x 128 halves each).  Separate
   // objects let the compiler tell the slots apart: a read of slot u then
   // waits only for the direct-to-LDS loads into slot u, not for every such
@@ -529,6 +546,27 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
   __shared__ __attribute__((aligned(1024))) uint16_t lds6[S > 6 ? kSlot : kNone];
   __shared__ __attribute__((aligned(1024))) uint16_t lds7[S > 7 ? kSlot : kNone];
   static_assert(S <= 8, "at most eight LDS slots");
+  constexpr int kRsSlot = RSIN ? WN * NP * RW : 1;
+  __shared__ __attribute__((aligned(256))) float rsl0[kRsSlot];
+  __shared__ __attribute__((aligned(256))) float rsl1[kRsSlot];
+  __shared__ __attribute__((aligned(256))) float rsl2[S > 2 ? kRsSlot : 1];
+  __shared__ __attribute__((aligned(256))) float rsl3[S > 3 ? kRsSlot : 1];
+  __shared__ __attribute__((aligned(256))) float rsl4[S > 4 ? kRsSlot : 1];
+  __shared__ __attribute__((aligned(256))) float rsl5[S > 5 ? kRsSlot : 1];
+  __shared__ __attribute__((aligned(256))) float rsl6[S > 6 ? kRsSlot : 1];
+  __shared__ __attribute__((aligned(256))) float rsl7[S > 7 ? kRsSlot : 1];
+  auto slot_rs = [&](int u) __attribute__((always_inline)) -> float* {
+    switch (u) {
+      case 0: return rsl0;
+      case 1: return rsl1;
+      case 2: return rsl2;
+      case 3: return rsl3;
+      case 4: return rsl4;
+      case 5: return rsl5;
+      case 6: return rsl6;
+      default: return rsl7;
+    }
+  };
   auto slot_lds = [&](int u) __attribute__((always_inline)) -> uint16_t* {
     switch (u) {
       case 0: return lds0;
@@ -623,6 +661,18 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
     for (int nt = 0; nt < NS; ++nt) r.w[nt] = wp[nt][b * 64];
 #pragma unroll
     for (int i = 0; i < NA; ++i) load_lds16(ap[i] + b * kTileK, slot_lds(slot) + 4 * (NA * wave + i) * kTileK);
+    if constexpr (RSIN) {
+      // lane l of load (p, h): the sum of row m0 + 64 h + l over period
+      // b NP + p (rows past M read row M - 1; never used)
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int h = 0; h < RW / 64; ++h) {
+          const int64_t row = m0 + 64 * h + lane;
+          load_lds4(rsum + (b * NP + p) * M + (row < M ? row : M - 1),
+                    slot_rs(slot) + (wave * NP + p) * RW + 64 * h);
+        }
+    }
   };
 
   f4 acc[MT][NS];
@@ -662,7 +712,12 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
         s_prev[nt] = s_cur;
       }
       f4 rs[MT];
-      if constexpr (BF16) {
+      if constexpr (RSIN) {
+        // rows 16 i + 4 quad .. + 3 of the tile (this wave's copy)
+        const float* rsp = slot_rs(slot) + (wave * NP + p) * RW + 4 * quad;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) rs[i] = *reinterpret_cast<const f4*>(rsp + 16 * i);
+      } else if constexpr (BF16) {
 #pragma unroll
         for (int i = 0; i < MT; ++i) rs[i] = f4{0.f, 0.f, 0.f, 0.f};
       }
@@ -672,7 +727,7 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
 #pragma unroll
         for (int i = 0; i < MT; ++i)
           a[i] = *reinterpret_cast<const u4*>(xa + 16 * i * kTileK + 8 * ((4 * j + quad) ^ c));
-        if constexpr (BF16) {
+        if constexpr (BF16 && !RSIN) {
 #pragma unroll
           for (int i = 0; i < MT; ++i) rs[i] = mfma<true>(a[i], ones, rs[i]);
         }
@@ -705,7 +760,7 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
   auto iterate = [&](int64_t b, int u) __attribute__((always_inline)) {
     const int un = (u + S - 1) % S;
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<C::kAfter>();
+    wait_vmcnt<kAfter>();
     lds_barrier();
     const int64_t bn = b + S - 1 < nb ? b + S - 1 : nb - 1;  // clamped: a redundant in-bounds load
     issue(kb0 + bn, rg[un], un);
@@ -869,9 +924,33 @@ struct Args {
   const int32_t* offs;  // grouped launch: expert row offsets [groups + 1], or nullptr
   int groups;           // grouped launch: experts (gridDim.z)
   int64_t max_rows;     // grouped launch: rows of the largest expert (grid height)
+  float* rsum;          // bf16 plain launches: workspace for the per-period row sums
+                        // [K / L][M] (L = 128 / periods per block), or nullptr
   int64_t M, K, N;
   int G, gs;
 };
+
+// rs[pd][m] = sum of x[m][pd L .. pd L + L - 1] in fp32 (bf16 x): the
+// zero-point term of the bf16 operand 128 + q, per scale period of L rows.
+// One thread per (row, period); consecutive threads read consecutive
+// periods of a row.
+__global__ void row_sums_bf16(const uint16_t* __restrict__ x, float* __restrict__ rs, int64_t M, int64_t K,
+                              int L) {
+  const int64_t P = K / L, total = M * P;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = idx / P, pd = idx - m * P;
+    const u4* src = reinterpret_cast<const u4*>(x + m * K + pd * L);
+    float sum = 0.f;
+    for (int c = 0; c < L / 8; ++c) {
+      const u4 v = src[c];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) sum += bit_as<float>(w[h] << 16) + bit_as<float>(w[h] & 0xFFFF0000u);
+    }
+    rs[pd * M + m] = sum;
+  }
+}
 
 // LDS bytes of a skinny launch: the reduction buffer, plus the staged
 // activation rows (at most kXlRows, row stride K + kXPad halves) when XL.
@@ -952,9 +1031,28 @@ hipError_t run_wide(const Args& a, const uint16_t* x, hipStream_t st) {
   const dim3 grid((unsigned)((T + NS * WN - 1) / (NS * WN)), (unsigned)((rows + C::BM - 1) / C::BM),
                   (unsigned)(a.offs != nullptr ? a.groups : splits));
   if (GR != (a.offs != nullptr)) return hipErrorInvalidValue;
-  gemm_wide<MT, NS, WN, S, GM, BF16, HZ, GR><<<grid, 64 * WN, 0, st>>>(
-      x, a.qw, a.sc, a.zs, a.bias, a.y, splits > 1 ? a.part : nullptr, a.offs, a.M, a.K, a.N, a.G);
-  hipError_t e = hipGetLastError();
+  hipError_t e = hipSuccess;
+  if constexpr (BF16 && !GR) {
+    if (a.rsum != nullptr) {
+      // the row sums of x per scale period first, then the kernel reads them
+      const int L = kTileK / Groups<GM>::kPeriods;
+      const int64_t total = a.M * (a.K / L);
+      int64_t blocks = (total + 255) / 256;
+      if (blocks > 65536) blocks = 65536;
+      row_sums_bf16<<<(unsigned)blocks, 256, 0, st>>>(x, a.rsum, a.M, a.K, L);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      gemm_wide<MT, NS, WN, S, GM, BF16, HZ, GR, true><<<grid, 64 * WN, 0, st>>>(
+          x, a.qw, a.sc, a.zs, a.bias, a.y, splits > 1 ? a.part : nullptr, a.offs, a.rsum, a.M, a.K, a.N, a.G);
+    } else {
+      gemm_wide<MT, NS, WN, S, GM, BF16, HZ, GR><<<grid, 64 * WN, 0, st>>>(
+          x, a.qw, a.sc, a.zs, a.bias, a.y, splits > 1 ? a.part : nullptr, a.offs, nullptr, a.M, a.K, a.N, a.G);
+    }
+  } else {
+    gemm_wide<MT, NS, WN, S, GM, BF16, HZ, GR><<<grid, 64 * WN, 0, st>>>(
+        x, a.qw, a.sc, a.zs, a.bias, a.y, splits > 1 ? a.part : nullptr, a.offs, nullptr, a.M, a.K, a.N, a.G);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int64_t total4 = a.M * a.N / 4;
   int64_t blocks = (total4 + 255) / 256;
