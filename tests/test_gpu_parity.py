@@ -515,27 +515,32 @@ def test_linear_wide_tiles_sampled(W, v):
 # HIP graph capture: replays match the eager launch bit for bit
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,K,gs,act", [(1, 1152, 128, True), (16, 1152, 128, True), (40, 1152, 128, True),
-                                        (300, 1152, 128, True), (1100, 1152, 128, True), (1, 1120, 32, False),
-                                        (40, 1120, 32, False), (300, 1120, 32, False), (1100, 1120, 32, False)])
-def test_linear_hip_graph_replays_match_eager(W, M, K, gs, act):
-    # act-order (gather into the workspace) and K tails (zero-padded copy
-    # into the workspace) inside a captured graph
+@pytest.mark.parametrize("M,K,gs,act,dtype", [(1, 1152, 128, True, "fp16"), (16, 1152, 128, True, "fp16"),
+                                              (40, 1152, 128, True, "fp16"), (300, 1152, 128, True, "fp16"),
+                                              (1100, 1152, 128, True, "fp16"), (1, 1120, 32, False, "fp16"),
+                                              (40, 1120, 32, False, "fp16"), (300, 1120, 32, False, "fp16"),
+                                              (1100, 1120, 32, False, "fp16"),
+                                              # bf16 row-sum pre-pass (with act-order and with a K tail)
+                                              (300, 1152, 128, True, "bf16"), (1100, 1120, 32, False, "bf16")])
+def test_linear_hip_graph_replays_match_eager(W, M, K, gs, act, dtype):
+    # act-order (gather into the workspace), K tails (zero-padded copy into
+    # the workspace) and the bf16 row sums (a pre-pass into the workspace)
+    # inside a captured graph
     import torch
     N = 4096
     G = K // gs
     rng = seeded(606, M, K)
     qweight = random_words(rng, (K // 8, N))
     qzeros = random_words(rng, (G, N // 8))
-    scales = uniform_scales(rng, (G, N), 0.002, 0.02, "fp16")
+    scales = uniform_scales(rng, (G, N), 0.002, 0.02, dtype)
     g_idx = actorder_gidx(rng, K, gs) if act else None
-    Lyr = _prepare(W, "std", K, N, gs, True, act, "fp16", qweight, qzeros, scales, g_idx)
-    say(f"graph M={M} K={K} g={gs} act={act} kernel={Lyr.kernel_name(M)}")
-    x = to_dev(normal_acts(seeded(607, M), (M, K), "fp16"))
+    Lyr = _prepare(W, "std", K, N, gs, True, act, dtype, qweight, qzeros, scales, g_idx)
+    say(f"graph M={M} K={K} g={gs} act={act} {dtype} kernel={Lyr.kernel_name(M)}")
+    x = to_dev(normal_acts(seeded(607, M), (M, K), dtype))
     t = Lyr.tiled
     ws_b = W.w4_workspace_size(Lyr.layer, M)
     ws = torch.zeros((max(ws_b, 1),), dtype=torch.uint8, device="cuda")
-    y_eager = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    y_eager = torch.empty((M, N), dtype=torch.float16 if dtype == "fp16" else torch.bfloat16, device="cuda")
     y_graph = torch.empty_like(y_eager)
 
     def call(y):
