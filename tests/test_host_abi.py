@@ -113,10 +113,16 @@ def test_launch_dims_follow_the_kernel_choice(W):
     L = W.make_layer(4096, 12288)
     assert W.w4_kernel_name(L, 1) == "w4_skinny_lds_k8"
     assert W.w4_launch_dims(L, 1) == ((768, 1, 1), 512)
-    # skinny, 16 waves, one strip per workgroup
+    # skinny, 16 waves, one strip per workgroup (M < 8 on a narrow layer)
     L = W.make_layer(4096, 4096)
-    assert W.w4_kernel_name(L, 16) == "w4_skinny_k16"
-    assert W.w4_launch_dims(L, 16) == ((256, 1, 1), 1024)
+    assert W.w4_kernel_name(L, 5) == "w4_skinny_k16"
+    assert W.w4_launch_dims(L, 5) == ((256, 1, 1), 1024)
+    # activation tiles through LDS: eight waves, one strip (narrow) or two
+    assert W.w4_kernel_name(L, 16) == "w4_skinny_dma_k8"
+    assert W.w4_launch_dims(L, 16) == ((256, 1, 1), 512)
+    L8 = W.make_layer(8192, 8192)
+    assert W.w4_kernel_name(L8, 9) == "w4_skinny_dma_n2_k8"
+    assert W.w4_launch_dims(L8, 9) == ((256, 1, 1), 512)
     # large M: one 1-D grid of 128 x 256 tiles of four waves
     L = W.make_layer(8192, 8192)
     assert W.w4_kernel_name(L, 2048) == "w4_big_128x256"

@@ -47,22 +47,25 @@ hipError_t launch_wide(const Shape& s, const GemmPlan& p, const Args& a0, void* 
   return wide_dispatch<false>(p.wide, s, a, x, st);
 }
 
-template <int MT, int NB, int KW, bool XL, bool BF16, bool HZ>
+template <int MT, int NB, int KW, bool XL, bool BF16, bool HZ, int D, bool AD>
 hipError_t pick_gm(const Args& a, hipStream_t st) {
   switch (group_mode(a.gs, a.K)) {
-    case GM_32: return run_skinny<MT, NB, KW, GM_32, BF16, HZ, XL>(a, st);
-    case GM_64: return run_skinny<MT, NB, KW, GM_64, BF16, HZ, XL>(a, st);
-    case GM_128: return run_skinny<MT, NB, KW, GM_128, BF16, HZ, XL>(a, st);
-    default: return run_skinny<MT, NB, KW, GM_CH, BF16, HZ, XL>(a, st);
+    case GM_32: return run_skinny<MT, NB, KW, GM_32, BF16, HZ, XL, D, AD>(a, st);
+    case GM_64: return run_skinny<MT, NB, KW, GM_64, BF16, HZ, XL, D, AD>(a, st);
+    case GM_128: return run_skinny<MT, NB, KW, GM_128, BF16, HZ, XL, D, AD>(a, st);
+    default: return run_skinny<MT, NB, KW, GM_CH, BF16, HZ, XL, D, AD>(a, st);
   }
 }
 
 // (act-order activations arrive gathered: the skinny kernels never see perm)
-template <int MT, int NB, int KW, bool XL>
+// D: ring depth (the measured default for the configuration unless given)
+template <int MT, int NB, int KW, bool XL, bool AD = false, int D = skinny_depth<MT, NB, KW, XL>()>
 hipError_t pick_flags(const Shape& s, const Args& a, hipStream_t st) {
   if (s.bf16)
-    return s.has_z ? pick_gm<MT, NB, KW, XL, true, true>(a, st) : pick_gm<MT, NB, KW, XL, true, false>(a, st);
-  return s.has_z ? pick_gm<MT, NB, KW, XL, false, true>(a, st) : pick_gm<MT, NB, KW, XL, false, false>(a, st);
+    return s.has_z ? pick_gm<MT, NB, KW, XL, true, true, D, AD>(a, st)
+                   : pick_gm<MT, NB, KW, XL, true, false, D, AD>(a, st);
+  return s.has_z ? pick_gm<MT, NB, KW, XL, false, true, D, AD>(a, st)
+                 : pick_gm<MT, NB, KW, XL, false, false, D, AD>(a, st);
 }
 
 }  // namespace
@@ -109,6 +112,17 @@ GemmPlan plan_tiles(const Shape& s, int64_t M) {
     const WideChoice& w = kWide[idx];
     p = GemmPlan{GemmKind::kWide, w.mt, w.ns, w.wn, false, w.name};
     p.wide = idx;
+  } else if (M <= 16 && ((T <= 256 && M >= 8) || (T > 256 && T % 2 == 0))) {
+    // each wave copies every block's activation tile into its own LDS ring
+    // slot with direct-to-LDS loads (whole rows) and reads its operands from
+    // there: loading them into registers touches 16 half-used cache lines per
+    // load, which measured 12-19% slower at M = 16 on the narrow layers
+    // (11008 x 4096: 13.6 -> 11.0 us; 4096 x 4096: 6.6 -> 5.8 us) and 15% at
+    // 8192 x 8192; eight waves, one strip per workgroup (ring 2) up to 256
+    // strips, else two strips (ring 3)
+    p = T <= 256 ? GemmPlan{GemmKind::kSkinny, 1, 1, 8, false, "w4_skinny_dma_k8"}
+                 : GemmPlan{GemmKind::kSkinny, 1, 2, 8, false, "w4_skinny_dma_n2_k8"};
+    p.ad = true;
   } else if (M <= 16) {
     // activations from registers; two strips per workgroup share them
     // (halving the activation traffic) unless N is small: then one strip
@@ -259,6 +273,7 @@ hipError_t launch_gemm(const Shape& s0, int64_t M, const void* x, const int32_t*
     a.perm = nullptr;
     sk.has_perm = false;
   }
+  if (p.ad) return p.nb == 2 ? pick_flags<1, 2, 8, false, true, 3>(sk, a, st) : pick_flags<1, 1, 8, false, true, 2>(sk, a, st);
   if (p.xl) return p.kw == 16 ? pick_flags<1, 1, 16, true>(sk, a, st) : pick_flags<1, 1, 8, true>(sk, a, st);
   if (p.nb == 2) return p.kw == 16 ? pick_flags<1, 2, 16, false>(sk, a, st) : pick_flags<1, 2, 8, false>(sk, a, st);
   return p.kw == 16 ? pick_flags<1, 1, 16, false>(sk, a, st) : pick_flags<1, 1, 8, false>(sk, a, st);

@@ -215,6 +215,41 @@ __device__ __forceinline__ void block_mac(f4 (&tot)[MT][NB], const u4 (&a)[MT][4
 constexpr int kXPad = 32;
 constexpr int kXlRows = 4;  // at most this many rows are staged (M <= 4)
 
+// Memory helpers shared by the kernels below.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at dst + 16 l (dst is wave-uniform).
+__device__ __forceinline__ void load_lds16(const uint16_t* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+
+// 4 bytes per lane: lane l's word lands at dst + l (dst is wave-uniform).
+__device__ __forceinline__ void load_lds4(const float* src, float* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
+}
+
+// Workgroup barrier for the pipeline.  __syncthreads() would add a release
+// fence, which waits for every outstanding direct-to-LDS load (they count as
+// LDS writes) and so drains the whole pipeline at every block.  Here each
+// wave has already waited for its own loads of the block about to be read
+// (wait_vmcnt), so the bare barrier suffices; the empty asm statements keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Registers of one 128-row block: weights, scales and zeros of NB strips,
 // and (unless the activations come from LDS) the A operands of MT row tiles.
 template <int MT, int NB, int NP, bool XL>
@@ -239,6 +274,7 @@ struct LaneView {
   const uint16_t* sc[NB];     // scale of column c of strip s, group 0
   const uint32_t* zs[NB];     // zero word holding column c of strip s, group 0
   const uint16_t* xr[MT];     // x row of tile i + 8 * quad
+  const uint16_t* xd[4];      // AD: source of this lane's 16 bytes in direct-to-LDS load i of a block
   const uint16_t* xl;         // XL: LDS row of this lane + 8 * quad
   bool row_ok[MT];            // row of tile i is < M
   int64_t nblk;
@@ -263,6 +299,24 @@ struct LaneView {
     }
     // LDS rows >= M are never staged; read row 0 instead
     xl = xlds + (row_ok[0] ? c : 0) * (K + kXPad) + 8 * quad;
+    // AD (one 16-row tile): load i of a block fills rows 4 i .. 4 i + 3 of
+    // the wave's 16 x 128 copy, lane l landing at chunk position l % 16 of
+    // row 4 i + l / 16, which holds logical chunk (l % 16) ^ row (rows >= M
+    // read row M - 1, never stored)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * i + quad;
+      int64_t m = m0 + row;
+      m = m < M ? m : M - 1;
+      xd[i] = x + m * K + 8 * (c ^ row);
+    }
+  }
+
+  // AD: the block's 16 x 128 activation tile into the wave's LDS copy dst
+  // (four 1 KiB direct-to-LDS loads, each of four whole 256-byte rows).
+  __device__ __forceinline__ void load_a_dma(int kb, uint16_t* dst) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_lds16(xd[i] + (int64_t)kb * kTileK, dst + 4 * i * kTileK);
   }
 
   // A operands of block kb straight from global memory.
@@ -282,7 +336,8 @@ struct LaneView {
   }
 
   // Weights, scales, zeros (and global A operands) of block b.
-  __device__ __forceinline__ void load_block(int b, BlockRegs<MT, NB, NP, XL>& r) const {
+  template <bool NOA>
+  __device__ __forceinline__ void load_block(int b, BlockRegs<MT, NB, NP, NOA>& r) const {
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
       r.wv[s] = w[s][(int64_t)b * 64];
@@ -293,12 +348,16 @@ struct LaneView {
         r.zraw[s][p] = HAS_Z ? zs[s][(int64_t)g * 2] : 0u;
       }
     }
-    if constexpr (!XL) load_a_global(b, r.a);
+    if constexpr (!NOA) load_a_global(b, r.a);
   }
 };
 
 // Skinny kernel: see the header comment.  XL: activations staged in LDS.
-template <int MT, int NB, int KW, int GM, bool BF16, bool HAS_Z, bool XL, int D>
+// AD: each wave copies every block's 16 x 128 activation tile into its own
+// LDS ring slot with direct-to-LDS loads (whole 256-byte rows, 8 cache lines
+// per load) and reads its MFMA operands from there; loading them straight
+// into registers instead touches 16 half-used lines per load.
+template <int MT, int NB, int KW, int GM, bool BF16, bool HAS_Z, bool XL, int D, bool AD = false>
 __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restrict__ x, const u4* __restrict__ qw,
                                                         const uint16_t* __restrict__ sc,
                                                         const uint32_t* __restrict__ zs,
@@ -306,6 +365,27 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
                                                         uint16_t* __restrict__ y, int64_t M, int64_t K, int64_t N,
                                                         int G) {
   static_assert(!XL || MT == 1, "LDS activations hold one 16-row tile");
+  static_assert(!AD || (MT == 1 && !XL && D <= 6), "per-block LDS activations: one 16-row tile, ring <= 6");
+  static_assert(!AD || (D - 1) * (NB + 4) < 64, "vmcnt is six bits");
+  // AD ring: one array per slot (so a read of slot u waits only for the
+  // loads into slot u), KW copies of 16 x 128 halves each
+  constexpr int kAdSlot = AD ? KW * 16 * kTileK : 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t ad0[kAdSlot];
+  __shared__ __attribute__((aligned(1024))) uint16_t ad1[AD && D > 1 ? kAdSlot : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t ad2[AD && D > 2 ? kAdSlot : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t ad3[AD && D > 3 ? kAdSlot : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t ad4[AD && D > 4 ? kAdSlot : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t ad5[AD && D > 5 ? kAdSlot : 8];
+  auto slot_ad = [&](int u) __attribute__((always_inline)) -> uint16_t* {
+    switch (u) {
+      case 0: return ad0;
+      case 1: return ad1;
+      case 2: return ad2;
+      case 3: return ad3;
+      case 4: return ad4;
+      default: return ad5;
+    }
+  };
   constexpr int NP = Groups<GM>::kPeriods;
   constexpr int R = MT * NB * 4;
   extern __shared__ float smem[];  // [KW][R][64] reduction buffer, then (XL) the activation rows
@@ -345,10 +425,24 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
   static_assert(D >= 2, "ring depth");
   const bool has_blocks = lo < hi;  // wave-uniform
   const int last = hi - 1;
-  BlockRegs<MT, NB, NP, XL> ring[D];
+  BlockRegs<MT, NB, NP, XL || AD> ring[D];
+  // the loads of block b into ring slot u (with AD also the activation tile
+  // into the wave's copy in LDS slot u, issued last).  kPerBlock is a lower
+  // bound on the loads one fill issues: the NB weight loads and the four
+  // direct-to-LDS loads; the scale and zero loads are left out because the
+  // compiler may merge them or hoist them out of the loop (per-channel
+  // scales), and leaving them out only makes the wait below longer.
+  constexpr int kPerBlock = NB + (AD ? 4 : 0);
+  auto fill = [&](int b, int u) __attribute__((always_inline)) {
+    v.load_block(b, ring[u]);
+    if constexpr (AD) v.load_a_dma(b, slot_ad(u) + wave * 16 * kTileK);
+  };
   if (has_blocks) {
 #pragma unroll
-    for (int u = 0; u < D - 1; ++u) v.load_block(lo + u < last ? lo + u : last, ring[u]);
+    for (int u = 0; u < D - 1; ++u) {
+      fill(lo + u < last ? lo + u : last, u);
+      if constexpr (AD) __builtin_amdgcn_sched_barrier(0);
+    }
   }
   if constexpr (XL) {
     // Stage the (at most kXlRows) activation rows: the loads of every row of
@@ -369,10 +463,19 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
     __syncthreads();
   }
 
-  auto compute = [&](int b, BlockRegs<MT, NB, NP, XL>& r) __attribute__((always_inline)) {
+  auto compute = [&](int b, int u) __attribute__((always_inline)) {
+    auto& r = ring[u];
     if constexpr (XL) {
       u4 a[MT][4];
       v.load_a_lds(b, a);
+      block_mac<MT, NB, GM, BF16, HAS_Z>(tot, a, r.wv, r.sraw, r.zraw, zshift, nm);
+    } else if constexpr (AD) {
+      // row c of the wave's copy, logical chunk 4 j + quad at (4 j + quad) ^ c
+      const int c = lane & 15, quad = lane >> 4;
+      const uint16_t* base = slot_ad(u) + wave * 16 * kTileK + c * kTileK;
+      u4 a[MT][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[0][j] = *reinterpret_cast<const u4*>(base + 8 * ((4 * j + quad) ^ c));
       block_mac<MT, NB, GM, BF16, HAS_Z>(tot, a, r.wv, r.sraw, r.zraw, zshift, nm);
     } else {
       block_mac<MT, NB, GM, BF16, HAS_Z>(tot, r.a, r.wv, r.sraw, r.zraw, zshift, nm);
@@ -384,13 +487,25 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
 #pragma unroll
       for (int u = 0; u < D; ++u) {
         const int nb = kb + u + D - 1;
-        v.load_block(nb < last ? nb : last, ring[(u + D - 1) % D]);
-        compute(kb + u, ring[u]);
+        fill(nb < last ? nb : last, (u + D - 1) % D);
+        if constexpr (AD) {
+          // block kb + u's activation tile has landed once at most the loads
+          // of the D - 1 later fills are outstanding (loads complete in issue
+          // order; the scheduling barriers keep the fills in block order and
+          // each fill's direct-to-LDS loads come after its register loads)
+          __builtin_amdgcn_sched_barrier(0);
+          wait_vmcnt<(D - 1) * kPerBlock>();
+        }
+        compute(kb + u, u);
+        if constexpr (AD) __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
     for (int u = 0; u < D - 1; ++u)
-      if (kb + u < hi) compute(kb + u, ring[u]);
+      if (kb + u < hi) {
+        if constexpr (AD) wait_vmcnt<0>();
+        compute(kb + u, u);
+      }
   }
 
   // Sum the KW waves' partial results in LDS, then bias, round and store.
@@ -464,39 +579,6 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
 // Rows >= M are staged from row M - 1 and never stored; strips >= N/16 read
 // strip 0 and are never stored.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
-// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes
-// land at dst + 16 l (dst is wave-uniform).
-__device__ __forceinline__ void load_lds16(const uint16_t* src, uint16_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
-}
-
-// 4 bytes per lane: lane l's word lands at dst + l (dst is wave-uniform).
-__device__ __forceinline__ void load_lds4(const float* src, float* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
-}
-
-// Workgroup barrier for the pipeline.  __syncthreads() would add a release
-// fence, which waits for every outstanding direct-to-LDS load (they count as
-// LDS writes) and so drains the whole pipeline at every block.  Here each
-// wave has already waited for its own loads of the block about to be read
-// (wait_vmcnt), so the bare barrier suffices; the empty asm statements keep
-// the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 template <int MT, int NS, int WN, int S>
 struct WideCfg {
@@ -971,7 +1053,8 @@ constexpr int skinny_depth() {
   return XL ? 2 : (MT * NB == 1 ? (KW >= 16 ? 3 : 6) : (MT * NB == 2 ? 3 : 2));
 }
 
-template <int MT, int NB, int KW, int GM, bool BF16, bool HZ, bool XL, int D = skinny_depth<MT, NB, KW, XL>()>
+template <int MT, int NB, int KW, int GM, bool BF16, bool HZ, bool XL, int D = skinny_depth<MT, NB, KW, XL>(),
+          bool AD = false>
 hipError_t run_skinny(const Args& a, hipStream_t st) {
   const int64_t T = (a.N + kTileN - 1) / kTileN;
   if (T % NB != 0) return hipErrorInvalidValue;
@@ -979,6 +1062,10 @@ hipError_t run_skinny(const Args& a, hipStream_t st) {
   if (XL && a.M > kXlRows) return hipErrorInvalidValue;  // staging holds kXlRows rows
   const size_t lds = skinny_lds_bytes(MT, NB, KW, XL, a.M, a.K);
   if (lds > kMaxSkinnyLds) return hipErrorInvalidValue;
+  // the AD ring is static LDS: D slots of KW 4 KiB copies, within the CU's 160 KiB with the rest
+  constexpr size_t kAdBytes = AD ? (size_t)D * KW * 16 * kTileK * sizeof(uint16_t) : 0;
+  static_assert(kAdBytes + (size_t)KW * MT * NB * 4 * 64 * sizeof(float) <= 160 * 1024, "AD ring LDS");
+  if (lds + kAdBytes > 160 * 1024) return hipErrorInvalidValue;
   if (lds > 64 * 1024) {
     // dynamic LDS beyond 64 KiB has to be allowed per kernel and device
     // (once each; devices past 64 are allowed on every call)
@@ -988,13 +1075,13 @@ hipError_t run_skinny(const Args& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
     if (bit == 0 || (allowed.load(std::memory_order_relaxed) & bit) == 0) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_skinny<MT, NB, KW, GM, BF16, HZ, XL, D>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_skinny<MT, NB, KW, GM, BF16, HZ, XL, D, AD>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxSkinnyLds);
       if (e != hipSuccess) return e;
       allowed.fetch_or(bit, std::memory_order_relaxed);
     }
   }
-  gemm_skinny<MT, NB, KW, GM, BF16, HZ, XL, D><<<grid, 64 * KW, lds, st>>>(
+  gemm_skinny<MT, NB, KW, GM, BF16, HZ, XL, D, AD><<<grid, 64 * KW, lds, st>>>(
       a.x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N, a.G);
   return hipGetLastError();
 }
