@@ -113,8 +113,11 @@ def test_launch_dims_follow_the_kernel_choice(W):
     L = W.make_layer(4096, 12288)
     assert W.w4_kernel_name(L, 1) == "w4_skinny_lds_k8"
     assert W.w4_launch_dims(L, 1) == ((768, 1, 1), 512)
-    # skinny, 16 waves, one strip per workgroup (M < 8 on a narrow layer)
+    # narrow layer, M <= 4: 16 waves, the activation rows copied per block
     L = W.make_layer(4096, 4096)
+    assert W.w4_kernel_name(L, 1) == "w4_skinny_dma4_k16"
+    assert W.w4_launch_dims(L, 4) == ((256, 1, 1), 1024)
+    # skinny, 16 waves, one strip per workgroup (M < 8 on a narrow layer)
     assert W.w4_kernel_name(L, 5) == "w4_skinny_k16"
     assert W.w4_launch_dims(L, 5) == ((256, 1, 1), 1024)
     # activation tiles through LDS: eight waves, one strip (narrow) or two

@@ -81,7 +81,8 @@ struct GemmPlan {
   int wide = 0;    // wide tile configuration (index into the kernel's table)
   int splits = 1;  // wide kernel: K ranges reduced by a second kernel (1 = none)
   bool rsin = false;  // bf16 wide kernel: row sums from a pre-pass instead of ones-operand MFMAs
-  bool ad = false;    // skinny kernel: activation tiles copied per block into LDS (direct-to-LDS loads)
+  int ar = 0;         // skinny kernel: rows of each block's activation tile copied into LDS
+                      // by direct-to-LDS loads (4 or 16; 0 = none)
 };
 
 GemmPlan plan_gemm(const Shape& s, int64_t M);

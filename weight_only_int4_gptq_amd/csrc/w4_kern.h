@@ -312,11 +312,13 @@ struct LaneView {
     }
   }
 
-  // AD: the block's 16 x 128 activation tile into the wave's LDS copy dst
-  // (four 1 KiB direct-to-LDS loads, each of four whole 256-byte rows).
+  // AD: the first AR rows (4 or 16) of the block's activation tile into the
+  // wave's LDS copy dst (AR / 4 direct-to-LDS loads of 1 KiB, each of four
+  // whole 256-byte rows).
+  template <int AR>
   __device__ __forceinline__ void load_a_dma(int kb, uint16_t* dst) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_lds16(xd[i] + (int64_t)kb * kTileK, dst + 4 * i * kTileK);
+    for (int i = 0; i < AR / 4; ++i) load_lds16(xd[i] + (int64_t)kb * kTileK, dst + 4 * i * kTileK);
   }
 
   // A operands of block kb straight from global memory.
@@ -357,7 +359,7 @@ struct LaneView {
 // LDS ring slot with direct-to-LDS loads (whole 256-byte rows, 8 cache lines
 // per load) and reads its MFMA operands from there; loading them straight
 // into registers instead touches 16 half-used lines per load.
-template <int MT, int NB, int KW, int GM, bool BF16, bool HAS_Z, bool XL, int D, bool AD = false>
+template <int MT, int NB, int KW, int GM, bool BF16, bool HAS_Z, bool XL, int D, int AR = 0>
 __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restrict__ x, const u4* __restrict__ qw,
                                                         const uint16_t* __restrict__ sc,
                                                         const uint32_t* __restrict__ zs,
@@ -365,17 +367,18 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
                                                         uint16_t* __restrict__ y, int64_t M, int64_t K, int64_t N,
                                                         int G) {
   static_assert(!XL || MT == 1, "LDS activations hold one 16-row tile");
-  static_assert(!AD || (MT == 1 && !XL && D <= 6), "per-block LDS activations: one 16-row tile, ring <= 6");
-  static_assert(!AD || (D - 1) * (NB + 4) < 64, "vmcnt is six bits");
+  static_assert(AR == 0 || ((AR == 4 || AR == 16) && MT == 1 && !XL && D <= 6),
+                "per-block LDS activations: 4 or 16 rows of one tile, ring <= 6");
+  static_assert((D - 1) * (NB + AR / 4) < 64, "vmcnt is six bits");
   // AD ring: one array per slot (so a read of slot u waits only for the
   // loads into slot u), KW copies of 16 x 128 halves each
-  constexpr int kAdSlot = AD ? KW * 16 * kTileK : 8;
+  constexpr int kAdSlot = AR ? KW * AR * kTileK : 8;
   __shared__ __attribute__((aligned(1024))) uint16_t ad0[kAdSlot];
-  __shared__ __attribute__((aligned(1024))) uint16_t ad1[AD && D > 1 ? kAdSlot : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t ad2[AD && D > 2 ? kAdSlot : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t ad3[AD && D > 3 ? kAdSlot : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t ad4[AD && D > 4 ? kAdSlot : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t ad5[AD && D > 5 ? kAdSlot : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t ad1[AR && D > 1 ? kAdSlot : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t ad2[AR && D > 2 ? kAdSlot : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t ad3[AR && D > 3 ? kAdSlot : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t ad4[AR && D > 4 ? kAdSlot : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t ad5[AR && D > 5 ? kAdSlot : 8];
   auto slot_ad = [&](int u) __attribute__((always_inline)) -> uint16_t* {
     switch (u) {
       case 0: return ad0;
@@ -425,23 +428,23 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
   static_assert(D >= 2, "ring depth");
   const bool has_blocks = lo < hi;  // wave-uniform
   const int last = hi - 1;
-  BlockRegs<MT, NB, NP, XL || AD> ring[D];
+  BlockRegs<MT, NB, NP, XL || AR != 0> ring[D];
   // the loads of block b into ring slot u (with AD also the activation tile
   // into the wave's copy in LDS slot u, issued last).  kPerBlock is a lower
   // bound on the loads one fill issues: the NB weight loads and the four
   // direct-to-LDS loads; the scale and zero loads are left out because the
   // compiler may merge them or hoist them out of the loop (per-channel
   // scales), and leaving them out only makes the wait below longer.
-  constexpr int kPerBlock = NB + (AD ? 4 : 0);
+  constexpr int kPerBlock = NB + AR / 4;
   auto fill = [&](int b, int u) __attribute__((always_inline)) {
     v.load_block(b, ring[u]);
-    if constexpr (AD) v.load_a_dma(b, slot_ad(u) + wave * 16 * kTileK);
+    if constexpr (AR != 0) v.template load_a_dma<AR>(b, slot_ad(u) + wave * AR * kTileK);
   };
   if (has_blocks) {
 #pragma unroll
     for (int u = 0; u < D - 1; ++u) {
       fill(lo + u < last ? lo + u : last, u);
-      if constexpr (AD) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (AR != 0) __builtin_amdgcn_sched_barrier(0);
     }
   }
   if constexpr (XL) {
@@ -469,13 +472,16 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
       u4 a[MT][4];
       v.load_a_lds(b, a);
       block_mac<MT, NB, GM, BF16, HAS_Z>(tot, a, r.wv, r.sraw, r.zraw, zshift, nm);
-    } else if constexpr (AD) {
-      // row c of the wave's copy, logical chunk 4 j + quad at (4 j + quad) ^ c
+    } else if constexpr (AR != 0) {
+      // row rr = min(c, AR - 1) of the wave's copy (with 4 rows, lanes past
+      // them read the last: rows >= M are never stored), logical chunk
+      // 4 j + quad at (4 j + quad) ^ rr
       const int c = lane & 15, quad = lane >> 4;
-      const uint16_t* base = slot_ad(u) + wave * 16 * kTileK + c * kTileK;
+      const int rr = c < AR ? c : AR - 1;
+      const uint16_t* base = slot_ad(u) + wave * AR * kTileK + rr * kTileK;
       u4 a[MT][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a[0][j] = *reinterpret_cast<const u4*>(base + 8 * ((4 * j + quad) ^ c));
+      for (int j = 0; j < 4; ++j) a[0][j] = *reinterpret_cast<const u4*>(base + 8 * ((4 * j + quad) ^ rr));
       block_mac<MT, NB, GM, BF16, HAS_Z>(tot, a, r.wv, r.sraw, r.zraw, zshift, nm);
     } else {
       block_mac<MT, NB, GM, BF16, HAS_Z>(tot, r.a, r.wv, r.sraw, r.zraw, zshift, nm);
@@ -488,7 +494,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
       for (int u = 0; u < D; ++u) {
         const int nb = kb + u + D - 1;
         fill(nb < last ? nb : last, (u + D - 1) % D);
-        if constexpr (AD) {
+        if constexpr (AR != 0) {
           // block kb + u's activation tile has landed once at most the loads
           // of the D - 1 later fills are outstanding (loads complete in issue
           // order; the scheduling barriers keep the fills in block order and
@@ -497,13 +503,13 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
           wait_vmcnt<(D - 1) * kPerBlock>();
         }
         compute(kb + u, u);
-        if constexpr (AD) __builtin_amdgcn_sched_barrier(0);
+        if constexpr (AR != 0) __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
     for (int u = 0; u < D - 1; ++u)
       if (kb + u < hi) {
-        if constexpr (AD) wait_vmcnt<0>();
+        if constexpr (AR != 0) wait_vmcnt<0>();
         compute(kb + u, u);
       }
   }
@@ -1054,7 +1060,7 @@ constexpr int skinny_depth() {
 }
 
 template <int MT, int NB, int KW, int GM, bool BF16, bool HZ, bool XL, int D = skinny_depth<MT, NB, KW, XL>(),
-          bool AD = false>
+          int AR = 0>
 hipError_t run_skinny(const Args& a, hipStream_t st) {
   const int64_t T = (a.N + kTileN - 1) / kTileN;
   if (T % NB != 0) return hipErrorInvalidValue;
@@ -1063,7 +1069,7 @@ hipError_t run_skinny(const Args& a, hipStream_t st) {
   const size_t lds = skinny_lds_bytes(MT, NB, KW, XL, a.M, a.K);
   if (lds > kMaxSkinnyLds) return hipErrorInvalidValue;
   // the AD ring is static LDS: D slots of KW 4 KiB copies, within the CU's 160 KiB with the rest
-  constexpr size_t kAdBytes = AD ? (size_t)D * KW * 16 * kTileK * sizeof(uint16_t) : 0;
+  constexpr size_t kAdBytes = (size_t)D * KW * AR * kTileK * sizeof(uint16_t);
   static_assert(kAdBytes + (size_t)KW * MT * NB * 4 * 64 * sizeof(float) <= 160 * 1024, "AD ring LDS");
   if (lds + kAdBytes > 160 * 1024) return hipErrorInvalidValue;
   if (lds > 64 * 1024) {
@@ -1075,13 +1081,13 @@ hipError_t run_skinny(const Args& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
     if (bit == 0 || (allowed.load(std::memory_order_relaxed) & bit) == 0) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_skinny<MT, NB, KW, GM, BF16, HZ, XL, D, AD>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_skinny<MT, NB, KW, GM, BF16, HZ, XL, D, AR>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxSkinnyLds);
       if (e != hipSuccess) return e;
       allowed.fetch_or(bit, std::memory_order_relaxed);
     }
   }
-  gemm_skinny<MT, NB, KW, GM, BF16, HZ, XL, D, AD><<<grid, 64 * KW, lds, st>>>(
+  gemm_skinny<MT, NB, KW, GM, BF16, HZ, XL, D, AR><<<grid, 64 * KW, lds, st>>>(
       a.x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N, a.G);
   return hipGetLastError();
 }
