@@ -292,6 +292,40 @@ def test_linear_small_shapes_all_m(W, v):
         _assert_close(ys[0], ref, dtype, f"{name} M={M}")
 
 
+# The two-strip skinny kernel with per-block LDS activation tiles runs layers
+# of 257..767 strips (even) at M = 5..16; N = 4352 is 272 strips.
+DMA_N2_VARIANTS = [
+    # (name, fmt, K, group_size, has_zeros, has_gidx, dtype)
+    ("std-fp16-g32-z", "std", 1152, 32, True, False, "fp16"),
+    ("std-bf16-g64-sym", "std", 1152, 64, False, False, "bf16"),
+    ("std-fp16-ch-z", "std", 1152, -1, True, False, "fp16"),
+    ("std-fp16-g128-z-act", "std", 1152, 128, True, True, "fp16"),
+    ("awq-bf16-g32-z-k1120", "awq", 1120, 32, True, False, "bf16"),
+]
+
+
+@pytest.mark.parametrize("v", DMA_N2_VARIANTS, ids=[v[0] for v in DMA_N2_VARIANTS])
+def test_linear_two_strip_lds_activations(W, v):
+    name, fmt, K, gs, has_z, has_g, dtype = v
+    N = 4352
+    G = 1 if gs == -1 else K // gs
+    rng = seeded(309, K, N, G, int(has_z), int(has_g), len(name))
+    lo, hi = (0.002, 0.02) if dtype == "fp16" else (0.001, 0.01)
+    qweight = random_words(rng, (K, N // 8) if fmt == "awq" else (K // 8, N))
+    qzeros = random_words(rng, (G, N // 8)) if has_z else None
+    scales = uniform_scales(rng, (G, N), lo, hi, dtype)
+    g_idx = actorder_gidx(rng, K, gs) if has_g else None
+    Lyr = _prepare(W, fmt, K, N, gs, has_z, has_g, dtype, qweight, qzeros, scales, g_idx)
+    for M in (5, 9, 16):
+        assert Lyr.kernel_name(M) == "w4_skinny_dma_n2_k8"
+        say(f"{name} M={M} kernel={Lyr.kernel_name(M)}")
+        x = normal_acts(seeded(310, M, K), (M, K), dtype)
+        ref = O.reference_linear(x, fmt, dtype, qweight, qzeros, scales, gs, g_idx=g_idx)
+        y, guard = _run_linear(W, Lyr, x, None, guard_rows=2)
+        assert (guard.view(np.uint16) == 0x7F7F).all(), "write past row M"
+        _assert_close(y, ref, dtype, f"{name} M={M} (all {M * N} outputs)")
+
+
 def test_linear_closed_forms(W):
     # constant codes c, zero z0, scale s0: y[m, n] = (c - z0) s0 sum_k x[m, k]
     K, N, gs = 512, 64, 128
