@@ -317,7 +317,7 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_f8(const uint8_t* __restrict_
 // summed in LDS in wave order (a fixed order: the result does not depend on
 // timing).  Rows >= M read row M - 1 and are never stored.
 // ---------------------------------------------------------------------------
-template <int KW, int D, bool PERCH, bool HAS_Z, bool BF16>
+template <int KW, int D, bool PERCH, bool HAS_Z, bool BF16, bool AD = false>
 __global__ __launch_bounds__(64 * KW) void gemm_f8_skinny(const uint8_t* __restrict__ xq,
                                                            const float* __restrict__ rs,
                                                            const float* __restrict__ xscale,
@@ -326,9 +326,31 @@ __global__ __launch_bounds__(64 * KW) void gemm_f8_skinny(const uint8_t* __restr
                                                            const uint16_t* __restrict__ bias,
                                                            uint16_t* __restrict__ y, int64_t M, int64_t Mr, int64_t K,
                                                            int64_t N, int G) {
-  static_assert(D >= 2, "ring depth");
+  static_assert(D >= 2 && (!AD || D <= 6), "ring depth");
+  static_assert(!AD || (D - 1) * 3 < 64, "vmcnt is six bits");
   constexpr int R = PERCH ? 8 : 4;  // partial tile (+ row-sum totals per channel)
   __shared__ float red[KW * R * 64];
+  // AD: each wave copies every block's 16 x 128-byte activation tile into its
+  // own slot of an LDS ring with two direct-to-LDS loads of eight whole rows
+  // each (16-byte chunk j of row r at position j ^ swz8(r)); loaded straight
+  // into registers, one A load touches 16 half-used cache lines
+  constexpr int kAd = AD ? KW * 16 * 128 : 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t ad0[kAd];
+  __shared__ __attribute__((aligned(1024))) uint8_t ad1[kAd];
+  __shared__ __attribute__((aligned(1024))) uint8_t ad2[AD && D > 2 ? kAd : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ad3[AD && D > 3 ? kAd : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ad4[AD && D > 4 ? kAd : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ad5[AD && D > 5 ? kAd : 16];
+  auto slot_ad = [&](int u) __attribute__((always_inline)) -> uint8_t* {
+    switch (u) {
+      case 0: return ad0;
+      case 1: return ad1;
+      case 2: return ad2;
+      case 3: return ad3;
+      case 4: return ad4;
+      default: return ad5;
+    }
+  };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, quad = lane >> 4;
@@ -344,6 +366,16 @@ __global__ __launch_bounds__(64 * KW) void gemm_f8_skinny(const uint8_t* __restr
   const int64_t m = c < M ? c : M - 1;
   const u4* ap = reinterpret_cast<const u4*>(xq + m * K + 32 * quad);
   const float* rp = rs + (4 * quad < Mr ? 4 * quad : Mr - 4);
+  // AD: load i of a block fills rows 8 i .. 8 i + 7 of the wave's copy; lane l
+  // lands at chunk position l % 8 of row 8 i + l / 8 and so loads logical
+  // chunk (l % 8) ^ swz8(row) (rows >= M read row M - 1, never stored)
+  const uint8_t* xd[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * i + (lane >> 3);
+    const int64_t mr = row < M ? row : M - 1;
+    xd[i] = xq + mr * K + 16 * ((lane & 7) ^ swz8(row));
+  }
 
   struct Blk {
     u4 w, a0, a1;
@@ -357,14 +389,33 @@ __global__ __launch_bounds__(64 * KW) void gemm_f8_skinny(const uint8_t* __restr
     r.s = sp[g * kTileN];
     r.z = HAS_Z ? zp[g * 2] : 0u;
     r.rsum = *reinterpret_cast<const f4*>(rp + (int64_t)b * Mr);
-    r.a0 = ap[(int64_t)b * 8];
-    r.a1 = ap[(int64_t)b * 8 + 1];
+    if constexpr (!AD) {
+      r.a0 = ap[(int64_t)b * 8];
+      r.a1 = ap[(int64_t)b * 8 + 1];
+    }
+  };
+  // the loads of block b into ring slot u, the activation copy last
+  auto fill = [&](int b, Blk& r, int u) __attribute__((always_inline)) {
+    load(b, r);
+    if constexpr (AD) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        load_lds16(reinterpret_cast<const uint16_t*>(xd[i] + (int64_t)b * 128),
+                   reinterpret_cast<uint16_t*>(slot_ad(u) + wave * 2048 + i * 1024));
+    }
   };
 
   f4 tot = {0.f, 0.f, 0.f, 0.f}, rsacc = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const Blk& r) __attribute__((always_inline)) {
-    const v8i a = {(int)r.a0.x, (int)r.a0.y, (int)r.a0.z, (int)r.a0.w,
-                   (int)r.a1.x, (int)r.a1.y, (int)r.a1.z, (int)r.a1.w};
+  auto compute = [&](const Blk& r, int u) __attribute__((always_inline)) {
+    u4 a0 = r.a0, a1 = r.a1;
+    if constexpr (AD) {
+      // row c of the wave's copy, chunks 2 quad and 2 quad + 1
+      const uint8_t* rowp = slot_ad(u) + wave * 2048 + c * 128;
+      a0 = *reinterpret_cast<const u4*>(rowp + 16 * ((2 * quad) ^ swz8(c)));
+      a1 = *reinterpret_cast<const u4*>(rowp + 16 * ((2 * quad + 1) ^ swz8(c)));
+    }
+    const v8i a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                   (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
     const uint32_t w4[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
     v8i bq;
 #pragma unroll
@@ -389,19 +440,33 @@ __global__ __launch_bounds__(64 * KW) void gemm_f8_skinny(const uint8_t* __restr
     const int last = hi - 1;
     Blk ring[D];
 #pragma unroll
-    for (int u = 0; u < D - 1; ++u) load(lo + u < last ? lo + u : last, ring[u]);
+    for (int u = 0; u < D - 1; ++u) {
+      fill(lo + u < last ? lo + u : last, ring[u], u);
+      if constexpr (AD) __builtin_amdgcn_sched_barrier(0);
+    }
     int kb = lo;
     for (; kb + D <= hi; kb += D) {
 #pragma unroll
       for (int u = 0; u < D; ++u) {
         const int nb = kb + u + D - 1;
-        load(nb < last ? nb : last, ring[(u + D - 1) % D]);
-        compute(ring[u]);
+        fill(nb < last ? nb : last, ring[(u + D - 1) % D], (u + D - 1) % D);
+        if constexpr (AD) {
+          // block kb + u's copy has landed once at most the loads of the
+          // D - 1 later fills are outstanding (a lower bound of 3 per fill:
+          // the weight load and the two copies; fills stay in block order)
+          __builtin_amdgcn_sched_barrier(0);
+          wait_vmcnt<(D - 1) * 3>();
+        }
+        compute(ring[u], u);
+        if constexpr (AD) __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
     for (int u = 0; u < D - 1; ++u)
-      if (kb + u < hi) compute(ring[u]);
+      if (kb + u < hi) {
+        if constexpr (AD) wait_vmcnt<0>();
+        compute(ring[u], u);
+      }
   }
 
 #pragma unroll
@@ -435,25 +500,25 @@ __global__ __launch_bounds__(64 * KW) void gemm_f8_skinny(const uint8_t* __restr
   }
 }
 
-template <int KW, int D, bool PERCH, bool HZ, bool BF16>
+template <int KW, int D, bool PERCH, bool HZ, bool BF16, bool AD>
 hipError_t run_f8_skinny(const Shape& s, int64_t M, const uint8_t* xq, const float* rs, const float* xscale,
                          const int32_t* tw, const void* ts, const int32_t* tz, const void* bias, void* y,
                          hipStream_t st) {
   if (M < 1 || M > 16) return hipErrorInvalidValue;
   const int64_t T = s.Np / kTileN;
-  gemm_f8_skinny<KW, D, PERCH, HZ, BF16><<<(unsigned)T, 64 * KW, 0, st>>>(
+  gemm_f8_skinny<KW, D, PERCH, HZ, BF16, AD><<<(unsigned)T, 64 * KW, 0, st>>>(
       xq, rs, xscale, reinterpret_cast<const u4*>(tw), static_cast<const uint16_t*>(ts),
       reinterpret_cast<const uint32_t*>(tz), static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), M,
       (int64_t)f8_rows(M), s.K, s.N, s.G);
   return hipGetLastError();
 }
 
-template <int KW, int D>
+template <int KW, int D, bool AD = false>
 hipError_t f8_skinny_flags(const Shape& s, int64_t M, const uint8_t* xq, const float* rs, const float* xscale,
                            const int32_t* tw, const void* ts, const int32_t* tz, const void* bias, void* y,
                            hipStream_t st) {
   const bool perch = s.Gp == 1;
-#define W4_F8S(P, Z, B) run_f8_skinny<KW, D, P, Z, B>(s, M, xq, rs, xscale, tw, ts, tz, bias, y, st)
+#define W4_F8S(P, Z, B) run_f8_skinny<KW, D, P, Z, B, AD>(s, M, xq, rs, xscale, tw, ts, tz, bias, y, st)
   if (s.bf16) {
     if (perch) return s.has_z ? W4_F8S(true, true, true) : W4_F8S(true, false, true);
     return s.has_z ? W4_F8S(false, true, true) : W4_F8S(false, false, true);
@@ -503,8 +568,10 @@ size_t f8_workspace_bytes(const Shape& s, int64_t M) {
 
 const char* f8_kernel_name(const Shape& s, int64_t M) {
   const int64_t T = s.Np / kTileN;
-  if (M <= 16 && T <= 256) return M <= 4 ? "w4a8_f8_skinny_k16" : "w4a8_f8_skinny_k8";
+  if (M <= 4 && T <= 256) return "w4a8_f8_skinny_k16";
   if (M <= 4 && T <= 1024) return "w4a8_f8_skinny_k8";
+  if (M <= 16 && T <= 256 && s.K <= 4096) return "w4a8_f8_skinny_dma_k16";
+  if (M <= 16 && T <= 1024) return "w4a8_f8_skinny_dma_k8";
   if (M <= 16) return "w4a8_f8_16x16";
   if (M <= 128) return "w4a8_f8_64x128";
   return "w4a8_f8_64x256";
@@ -539,13 +606,16 @@ hipError_t launch_f8_gemm(const Shape& s, int64_t M, const uint8_t* xq, const fl
   // kernel with 8 waves at M <= 4; otherwise one wave walking all of K per
   // 16 columns.  Prefill: 64 x 256 tiles of four waves (each 64 x 64), which
   // measured fastest among the 64- and 128-row shapes at 2048 and 8192 rows.
+  // Above 4 rows the K-split kernels copy each block's activation tile into
+  // LDS (whole rows per load): 13-19% faster at M = 16 than loading the
+  // operands into registers.
   const int64_t T = s.Np / kTileN;
-  if (M <= 16 && T <= 256) {
-    if (M <= 4) return f8_skinny_flags<16, 3>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
-    return f8_skinny_flags<8, 6>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
-  }
-  if (M <= 4 && T <= 1024)
-    return f8_skinny_flags<8, 2>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+  if (M <= 4 && T <= 256) return f8_skinny_flags<16, 3>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+  if (M <= 4 && T <= 1024) return f8_skinny_flags<8, 2>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+  if (M <= 16 && T <= 256 && s.K <= 4096)
+    return f8_skinny_flags<16, 3, true>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+  if (M <= 16 && T <= 1024)
+    return f8_skinny_flags<8, 3, true>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
   if (M <= 16) return f8_flags<1, 1, 1, 4>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
   if (M <= 128) return f8_flags<4, 2, 4, 3>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
   return f8_flags<4, 4, 4, 2>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
