@@ -473,15 +473,16 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
       v.load_a_lds(b, a);
       block_mac<MT, NB, GM, BF16, HAS_Z>(tot, a, r.wv, r.sraw, r.zraw, zshift, nm);
     } else if constexpr (AR != 0) {
-      // row rr = min(c, AR - 1) of the wave's copy (with 4 rows, lanes past
-      // them read the last: rows >= M are never stored), logical chunk
-      // 4 j + quad at (4 j + quad) ^ rr
+      // row c % AR of the wave's copy, chunk position (4 j + quad) ^ c: for
+      // c < AR that is logical chunk 4 j + quad of row c; with 4 rows the
+      // lanes past them (rows >= M, never stored) read some other chunk, at
+      // a position of their own, so the 16 lanes of a quad hit 16 distinct
+      // 16-byte bank groups
       const int c = lane & 15, quad = lane >> 4;
-      const int rr = c < AR ? c : AR - 1;
-      const uint16_t* base = slot_ad(u) + wave * AR * kTileK + rr * kTileK;
+      const uint16_t* base = slot_ad(u) + wave * AR * kTileK + (c & (AR - 1)) * kTileK;
       u4 a[MT][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a[0][j] = *reinterpret_cast<const u4*>(base + 8 * ((4 * j + quad) ^ rr));
+      for (int j = 0; j < 4; ++j) a[0][j] = *reinterpret_cast<const u4*>(base + 8 * ((4 * j + quad) ^ c));
       block_mac<MT, NB, GM, BF16, HAS_Z>(tot, a, r.wv, r.sraw, r.zraw, zshift, nm);
     } else {
       block_mac<MT, NB, GM, BF16, HAS_Z>(tot, r.a, r.wv, r.sraw, r.zraw, zshift, nm);
