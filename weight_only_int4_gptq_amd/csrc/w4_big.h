@@ -188,25 +188,26 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) s_prev[nt] = 1.f;
 
+  // Each row tile's rescale is applied just before its first MFMA of the
+  // period, and the scheduler is asked to issue the 16 multiplies of one
+  // tile after the MFMA of the tile before it: the matrix core works through
+  // that MFMA while the vector ALU rescales the next tile, instead of all
+  // 16 MT NT multiplies running ahead of the period's first MFMA.
+  constexpr bool RESCALE = GM != GM_CH;
   auto compute = [&](const Slot& r, int slot) __attribute__((always_inline)) {
     // row of this lane in row tile i: 32 (MT wm + i) + c, so row % 16 == c % 16
     const uint16_t* xa = slot_lds(slot) + (wm * MT * 32 + c) * kTileK;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       uint32_t n1[NT], n2[NT];
+      float ratio[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const uint32_t z = HAS_Z ? (r.z[nt][p] >> zshift) & 0xFu : 8u;
         n1[nt] = nz1024_bits(z);
         n2[nt] = nz64_bits(z);
         const float s_cur = act_to_f32<false>(r.s[nt][p]);
-        if constexpr (GM != GM_CH) {
-          const float ratio = s_prev[nt] * __builtin_amdgcn_rcpf(s_cur);
-#pragma unroll
-          for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][nt][q] *= ratio;
-        }
+        ratio[nt] = s_prev[nt] * __builtin_amdgcn_rcpf(s_cur);
         s_prev[nt] = s_cur;
       }
 #pragma unroll
@@ -221,7 +222,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
           const uint32_t w = r.w[nt][step & 1][step >> 1];
           const u4 bq = dq_f16(w, n1[nt], n2[nt], nm);
 #pragma unroll
-          for (int i = 0; i < MT; ++i) acc[i][nt] = mfma32(a[i], bq, acc[i][nt]);
+          for (int i = 0; i < MT; ++i) {
+            if (RESCALE && st == 0) {
+#pragma unroll
+              for (int q = 0; q < 16; ++q) acc[i][nt][q] *= ratio[nt];
+            }
+            acc[i][nt] = mfma32(a[i], bq, acc[i][nt]);
+          }
+        }
+        if (RESCALE && st == 0) {
+#pragma unroll
+          for (int t = 0; t < MT * NT; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x0002, 16, 0);  // 16 VALU: one tile's rescale
+            __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // then its MFMA
+          }
         }
       }
     }
