@@ -326,6 +326,31 @@ def test_linear_two_strip_lds_activations(W, v):
         _assert_close(y, ref, dtype, f"{name} M={M} (all {M * N} outputs)")
 
 
+# The three-strip variant runs 513..768 strips divisible by three at
+# M <= 16 (M >= 5 where the activation rows are not staged); N = 9216 is 576
+# strips, 192 workgroups.
+@pytest.mark.parametrize("v", DMA_N2_VARIANTS, ids=[v[0] for v in DMA_N2_VARIANTS])
+def test_linear_three_strip_lds_activations(W, v):
+    name, fmt, K, gs, has_z, has_g, dtype = v
+    N = 9216
+    G = 1 if gs == -1 else K // gs
+    rng = seeded(311, K, N, G, int(has_z), int(has_g), len(name))
+    lo, hi = (0.002, 0.02) if dtype == "fp16" else (0.001, 0.01)
+    qweight = random_words(rng, (K, N // 8) if fmt == "awq" else (K // 8, N))
+    qzeros = random_words(rng, (G, N // 8)) if has_z else None
+    scales = uniform_scales(rng, (G, N), lo, hi, dtype)
+    g_idx = actorder_gidx(rng, K, gs) if has_g else None
+    Lyr = _prepare(W, fmt, K, N, gs, has_z, has_g, dtype, qweight, qzeros, scales, g_idx)
+    for M in (5, 9, 16):
+        assert Lyr.kernel_name(M) == "w4_skinny_dma_n3_k8"
+        say(f"{name} M={M} kernel={Lyr.kernel_name(M)}")
+        x = normal_acts(seeded(312, M, K), (M, K), dtype)
+        ref = O.reference_linear(x, fmt, dtype, qweight, qzeros, scales, gs, g_idx=g_idx)
+        y, guard = _run_linear(W, Lyr, x, None, guard_rows=2)
+        assert (guard.view(np.uint16) == 0x7F7F).all(), "write past row M"
+        _assert_close(y, ref, dtype, f"{name} M={M} (all {M * N} outputs)")
+
+
 def test_linear_closed_forms(W):
     # constant codes c, zero z0, scale s0: y[m, n] = (c - z0) s0 sum_k x[m, k]
     K, N, gs = 512, 64, 128

@@ -126,6 +126,17 @@ def test_launch_dims_follow_the_kernel_choice(W):
     L8 = W.make_layer(8192, 8192)
     assert W.w4_kernel_name(L8, 9) == "w4_skinny_dma_n2_k8"
     assert W.w4_launch_dims(L8, 9) == ((256, 1, 1), 512)
+    # three strips per workgroup on 513..768 strips divisible by three (one
+    # round of at most 256 workgroups), else the shared-tile 16-row kernel
+    L = W.make_layer(4096, 12288)
+    assert W.w4_kernel_name(L, 16) == "w4_skinny_dma_n3_k8"
+    assert W.w4_launch_dims(L, 16) == ((256, 1, 1), 512)
+    assert W.w4_kernel_name(W.make_layer(4096, 9216), 9) == "w4_skinny_dma_n3_k8"
+    assert W.w4_launch_dims(W.make_layer(4096, 9216), 9) == ((192, 1, 1), 512)
+    L = W.make_layer(4096, 10240)
+    assert W.w4_kernel_name(L, 16) == "w4_wide_16x64_w4"
+    assert W.w4_launch_dims(L, 16) == ((160, 1, 1), 256)
+    assert W.w4_kernel_name(W.make_layer(4096, 22016), 8) == "w4_wide_16x32_w2"
     # large M: one 1-D grid of 128 x 256 tiles of four waves
     L = W.make_layer(8192, 8192)
     assert W.w4_kernel_name(L, 2048) == "w4_big_128x256"

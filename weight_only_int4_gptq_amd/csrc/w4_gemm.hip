@@ -107,25 +107,34 @@ GemmPlan plan_tiles(const Shape& s, int64_t M) {
   } else if (M <= 4 && skinny_lds_bytes(1, 1, 8, true, M, s.K) <= kMaxSkinnyLds) {
     // activations staged in LDS once per workgroup
     p = GemmPlan{GemmKind::kSkinny, 1, 1, 8, true, "w4_skinny_lds_k8"};
-  } else if (M <= 16 && T >= 768) {
-    // many strips (N >= 12288): every wave walks all of K for one strip with
+  } else if (M <= 16 && T > 512 && !(T <= 768 && T % 3 == 0)) {
+    // many strips (N > 8192): every wave walks all of K for one strip with
     // the activation tile in LDS shared by the workgroup's waves (four for
     // up to 1024 strips, else two with a six-deep pipeline), which measured
-    // faster than splitting K
+    // faster than splitting K, and than the per-wave kernels below once
+    // those would need a second round of workgroups (10240 x 4096 at
+    // M = 16: 14.0 -> 10.7 us)
     const int idx = T <= 1024 ? kWide16x64w4 : kWide16x32w2;
     const WideChoice& w = kWide[idx];
     p = GemmPlan{GemmKind::kWide, w.mt, w.ns, w.wn, false, w.name};
     p.wide = idx;
-  } else if (M <= 16 && ((T <= 256 && M >= 8) || (T > 256 && T % 2 == 0))) {
+  } else if (M <= 16 && ((T <= 256 && M >= 8) || (T > 256 && T <= 512 && T % 2 == 0) || T > 512)) {
     // each wave copies every block's activation tile into its own LDS ring
     // slot with direct-to-LDS loads (whole rows) and reads its operands from
     // there: loading them into registers touches 16 half-used cache lines per
     // load, which measured 12-19% slower at M = 16 on the narrow layers
     // (11008 x 4096: 13.6 -> 11.0 us; 4096 x 4096: 6.6 -> 5.8 us) and 15% at
-    // 8192 x 8192; eight waves, one strip per workgroup (ring 2) up to 256
-    // strips, else two strips (ring 3)
-    p = T <= 256 ? GemmPlan{GemmKind::kSkinny, 1, 1, 8, false, "w4_skinny_dma_k8"}
-                 : GemmPlan{GemmKind::kSkinny, 1, 2, 8, false, "w4_skinny_dma_n2_k8"};
+    // 8192 x 8192.  Eight waves; the ring and the reduction take one CU's
+    // LDS, so the strips per workgroup keep the grid to one round of at most
+    // 256 workgroups: one strip (ring 2) up to 256 strips, two (ring 3) up
+    // to 512, three (ring 3) up to 768 (12288: 10.9 -> 10.3 us against the
+    // shared-tile kernel above; 9216: 13.7 -> 9.5 us against two strips)
+    if (T <= 256)
+      p = GemmPlan{GemmKind::kSkinny, 1, 1, 8, false, "w4_skinny_dma_k8"};
+    else if (T <= 512)
+      p = GemmPlan{GemmKind::kSkinny, 1, 2, 8, false, "w4_skinny_dma_n2_k8"};
+    else
+      p = GemmPlan{GemmKind::kSkinny, 1, 3, 8, false, "w4_skinny_dma_n3_k8"};
     p.ar = 16;
   } else if (M <= 16) {
     // activations from registers; two strips per workgroup share them
@@ -278,7 +287,10 @@ hipError_t launch_gemm(const Shape& s0, int64_t M, const void* x, const int32_t*
     sk.has_perm = false;
   }
   if (p.ar == 4) return pick_flags<1, 1, 16, false, 4, 3>(sk, a, st);
-  if (p.ar == 16) return p.nb == 2 ? pick_flags<1, 2, 8, false, 16, 3>(sk, a, st) : pick_flags<1, 1, 8, false, 16, 2>(sk, a, st);
+  if (p.ar == 16) {
+    if (p.nb == 3) return pick_flags<1, 3, 8, false, 16, 3>(sk, a, st);
+    return p.nb == 2 ? pick_flags<1, 2, 8, false, 16, 3>(sk, a, st) : pick_flags<1, 1, 8, false, 16, 2>(sk, a, st);
+  }
   if (p.xl) return pick_flags<1, 1, 8, true>(sk, a, st);
   if (p.nb == 2) return p.kw == 16 ? pick_flags<1, 2, 16, false>(sk, a, st) : pick_flags<1, 2, 8, false>(sk, a, st);
   return p.kw == 16 ? pick_flags<1, 1, 16, false>(sk, a, st) : pick_flags<1, 1, 8, false>(sk, a, st);
