@@ -38,13 +38,6 @@ __device__ __forceinline__ f4 mfma_f8(const v8i& a, const v8i& b, f4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kE8m0One, 0, kE8m0Code);
 }
 
-// E4M3 value of a byte (finite bytes only), for the row sums
-__device__ __forceinline__ float e4m3_value(uint32_t b) {
-  const uint32_t e = (b >> 3) & 0xF, m = b & 7;
-  const float mag = e == 0 ? (float)m * 0.001953125f : __builtin_ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
-  return (b & 0x80) ? -mag : mag;
-}
-
 // ---------------------------------------------------------------------------
 // Activation quantization: one thread per 8 consecutive (sorted) columns.
 // xq [M][Kp] in operand order; rs [Kp/128][Mr] fp32 block sums of the
@@ -52,10 +45,13 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
 // to a multiple of 4 (rows M .. Mr - 1 are zero); columns K .. Kp - 1 of a
 // K tail are zero.
 // ---------------------------------------------------------------------------
-template <bool BF16, bool PERM>
+// VEC (no perm, K % 8 == 0, x 16-byte aligned): the 8 columns arrive in one
+// 16-byte load; otherwise one 2-byte load per column.
+template <bool BF16, bool PERM, bool VEC>
 __global__ void quant_fp8(const uint16_t* __restrict__ x, const float* __restrict__ xscale,
                           const int32_t* __restrict__ perm, uint8_t* __restrict__ xq, float* __restrict__ rs,
                           int64_t M, int64_t Mr, int64_t K, int64_t Kp) {
+  static_assert(!(VEC && PERM), "the gathered order has no contiguous 8-column chunks");
   const int64_t chunks = Kp / 8;  // per row; 16 per 128-column block
   const int64_t total = Mr * chunks;  // a multiple of 16
   const float s = xscale[0];
@@ -66,28 +62,56 @@ __global__ void quant_fp8(const uint16_t* __restrict__ x, const float* __restric
     const int64_t m = idx / chunks, cc = idx - m * chunks;
     const int64_t k0 = 8 * cc;
     const uint16_t* row = x + m * K;
-    uint32_t codes[8];
+    // v[i]: column k0 + S[i] of the sorted order, S = [0,4,1,5,2,6,3,7]
+    float v[8];
+    if constexpr (VEC) {
+      uint16_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (m < M && k0 < K) {
+        const u4 raw = *reinterpret_cast<const u4*>(row + k0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h[2 * j] = (uint16_t)(raw[j] & 0xFFFFu);
+          h[2 * j + 1] = (uint16_t)(raw[j] >> 16);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = (i & 1) ? 4 + (i >> 1) : (i >> 1);
+        v[i] = act_to_f32<BF16>(h[j]) / s;  // IEEE fp32 division
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t k = k0 + ((i & 1) ? 4 + (i >> 1) : (i >> 1));
+        v[i] = 0.f;
+        if (m < M && k < K) {
+          const uint32_t src = PERM ? (uint32_t)perm[k] : (uint32_t)k;
+          v[i] = act_to_f32<BF16>(row[src < (uint32_t)K ? src : 0u]) / s;  // IEEE fp32 division
+        }
+      }
+    }
+    // codes two at a time (round to nearest even), four per 32-bit word
+    uint32_t word[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      float c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = __builtin_fminf(__builtin_fmaxf(v[4 * w + i], -448.f), 448.f);
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+      word[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+    }
+    // the exact E4M3 values, summed in the sorted order
+    const int w0 = (int)word[0], w1 = (int)word[1];
+    const float e[8] = {__builtin_amdgcn_cvt_f32_fp8(w0, 0), __builtin_amdgcn_cvt_f32_fp8(w0, 1),
+                        __builtin_amdgcn_cvt_f32_fp8(w0, 2), __builtin_amdgcn_cvt_f32_fp8(w0, 3),
+                        __builtin_amdgcn_cvt_f32_fp8(w1, 0), __builtin_amdgcn_cvt_f32_fp8(w1, 1),
+                        __builtin_amdgcn_cvt_f32_fp8(w1, 2), __builtin_amdgcn_cvt_f32_fp8(w1, 3)};
     float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // column k0 + S[i] of the sorted order, S = [0,4,1,5,2,6,3,7]
-      const int64_t k = k0 + ((i & 1) ? 4 + (i >> 1) : (i >> 1));
-      float v = 0.f;
-      if (m < M && k < K) {
-        const uint32_t src = PERM ? (uint32_t)perm[k] : (uint32_t)k;
-        v = act_to_f32<BF16>(row[src < (uint32_t)K ? src : 0u]) / s;  // IEEE fp32 division
-      }
-      v = __builtin_fminf(__builtin_fmaxf(v, -448.f), 448.f);
-      codes[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false) & 0xFFu;
-      sum += e4m3_value(codes[i]);
-    }
+    for (int i = 0; i < 8; ++i) sum += e[i];
     // operand order: chunk cc of its block -> (j, q) = (cc % 16 / 4, cc % 4)
     const int64_t b = cc / 16, c16 = cc % 16;
-    if (m < M) {
-      const uint32_t lo = codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24);
-      const uint32_t hi = codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24);
-      *reinterpret_cast<uint2*>(xq + m * Kp + 128 * b + 32 * (c16 % 4) + 8 * (c16 / 4)) = make_uint2(lo, hi);
-    }
+    if (m < M) *reinterpret_cast<uint2*>(xq + m * Kp + 128 * b + 32 * (c16 % 4) + 8 * (c16 / 4)) = make_uint2(word[0], word[1]);
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) sum += __shfl_xor(sum, d, 16);
     if (c16 == 0) rs[b * Mr + m] = sum;
@@ -585,13 +609,16 @@ hipError_t launch_f8_quantize(const Shape& s, int64_t M, const void* x, const fl
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   const uint16_t* xx = static_cast<const uint16_t*>(x);
-#define W4_Q(B, P) quant_fp8<B, P><<<(unsigned)blocks, 256, 0, st>>>(xx, xscale, perm, xq, rs, M, Mr, s.K, s.Kp)
+  const bool vec = s.K % 8 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0;
+#define W4_Q(B, P, V) quant_fp8<B, P, V><<<(unsigned)blocks, 256, 0, st>>>(xx, xscale, perm, xq, rs, M, Mr, s.K, s.Kp)
   if (s.bf16) {
-    if (perm) W4_Q(true, true);
-    else W4_Q(true, false);
+    if (perm) W4_Q(true, true, false);
+    else if (vec) W4_Q(true, false, true);
+    else W4_Q(true, false, false);
   } else {
-    if (perm) W4_Q(false, true);
-    else W4_Q(false, false);
+    if (perm) W4_Q(false, true, false);
+    else if (vec) W4_Q(false, false, true);
+    else W4_Q(false, false, false);
   }
 #undef W4_Q
   return hipGetLastError();
