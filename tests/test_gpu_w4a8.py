@@ -96,8 +96,10 @@ LINEAR_CASES = [
     ("std-fp16-g128-z-act", "std", 512, 272, 128, True, True, "fp16", True, SX),
     ("std-fp16-ch-z", "std", 384, 272, -1, True, False, "fp16", False, SX),
     ("std-bf16-ch-sym-k224", "std", 224, 40, -1, False, False, "bf16", True, SX_SMALL),
+    # 272 strips: the four-wave K-split kernel with LDS activation tiles at M <= 4
+    ("awq-fp16-g128-n4352", "awq", 640, 4352, 128, True, False, "fp16", True, SX),
 ]
-LINEAR_MS = (1, 5, 16, 17, 64, 130, 300)
+LINEAR_MS = (1, 4, 5, 16, 17, 64, 130, 300)
 
 
 def _check(y_bits, ref, dtype, what):
@@ -127,7 +129,7 @@ def test_w4a8_linear_matches_the_oracle(W, v):
 
 FULL_CASES = [
     # workload shapes with fp8 activations: (label, fmt, K, N, gs, has_z, act, dtype, Ms)
-    ("decode-awq-fp16", "awq", 4096, 12288, 128, True, False, "fp16", (1, 16)),
+    ("decode-awq-fp16", "awq", 4096, 12288, 128, True, False, "fp16", (1, 4, 16)),
     ("decode-down-awq-fp16", "awq", 11008, 4096, 128, True, False, "fp16", (1, 4, 16)),
     ("mid-std-bf16-sym", "std", 8192, 8192, 128, False, False, "bf16", (64, 256)),
     ("prefill-awq-fp16", "awq", 8192, 8192, 128, True, False, "fp16", (2048,)),

@@ -154,7 +154,8 @@ def test_w4a8_kernel_choice(W):
     assert W.w4a8_kernel_name(W.make_layer(4096, 4096), 1) == "w4a8_f8_skinny_k16"
     assert W.w4a8_kernel_name(W.make_layer(11008, 4096), 16) == "w4a8_f8_skinny_dma_k8"
     assert W.w4a8_kernel_name(W.make_layer(4096, 4096), 16) == "w4a8_f8_skinny_dma_k16"
-    assert W.w4a8_kernel_name(W.make_layer(4096, 12288), 4) == "w4a8_f8_skinny_k8"
+    assert W.w4a8_kernel_name(W.make_layer(4096, 12288), 4) == "w4a8_f8_skinny_dma_k4"
+    assert W.w4a8_kernel_name(W.make_layer(11008, 4096), 1) == "w4a8_f8_skinny_k16_r2"
     assert W.w4a8_kernel_name(W.make_layer(4096, 12288), 16) == "w4a8_f8_skinny_dma_k8"
     assert W.w4a8_kernel_name(W.make_layer(4096, 22016), 1) == "w4a8_f8_16x16"
     assert W.w4a8_kernel_name(W.make_layer(8192, 8192), 64) == "w4a8_f8_64x128"

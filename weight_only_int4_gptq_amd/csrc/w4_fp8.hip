@@ -592,8 +592,8 @@ size_t f8_workspace_bytes(const Shape& s, int64_t M) {
 
 const char* f8_kernel_name(const Shape& s, int64_t M) {
   const int64_t T = s.Np / kTileN;
-  if (M <= 4 && T <= 256) return "w4a8_f8_skinny_k16";
-  if (M <= 4 && T <= 1024) return "w4a8_f8_skinny_k8";
+  if (M <= 4 && T <= 256) return s.K <= 4096 ? "w4a8_f8_skinny_k16" : "w4a8_f8_skinny_k16_r2";
+  if (M <= 4 && T <= 1024) return "w4a8_f8_skinny_dma_k4";
   if (M <= 16 && T <= 256 && s.K <= 4096) return "w4a8_f8_skinny_dma_k16";
   if (M <= 16 && T <= 1024) return "w4a8_f8_skinny_dma_k8";
   if (M <= 16) return "w4a8_f8_16x16";
@@ -628,17 +628,22 @@ hipError_t launch_f8_gemm(const Shape& s, int64_t M, const uint8_t* xq, const fl
                           const int32_t* tiled_w, const void* tiled_s, const int32_t* tiled_z, const void* bias,
                           void* y, hipStream_t st) {
   // Decode rows (M <= 16), from timing sweeps of the 7B-class decode layers:
-  // up to 256 strips (N <= 4096), the K-split kernel (16 waves, 3-deep ring
-  // up to 4 rows; 8 waves, 6-deep above); up to 1024 strips, the K-split
-  // kernel with 8 waves at M <= 4; otherwise one wave walking all of K per
-  // 16 columns.  Prefill: 64 x 256 tiles of four waves (each 64 x 64), which
+  // up to 256 strips (N <= 4096), the K-split kernel (16 waves up to 4
+  // rows); up to 1024 strips, the K-split kernel with 4 waves at M <= 4;
+  // otherwise one wave walking all of K per 16 columns.  Prefill: 64 x 256 tiles of four waves (each 64 x 64), which
   // measured fastest among the 64- and 128-row shapes at 2048 and 8192 rows.
   // Above 4 rows the K-split kernels copy each block's activation tile into
   // LDS (whole rows per load): 13-19% faster at M = 16 than loading the
   // operands into registers.
   const int64_t T = s.Np / kTileN;
-  if (M <= 4 && T <= 256) return f8_skinny_flags<16, 3>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
-  if (M <= 4 && T <= 1024) return f8_skinny_flags<8, 2>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+  if (M <= 4 && T <= 256) {
+    // two blocks per wave at K = 4096 fit a 3-deep ring; longer K ran 6-7%
+    // faster with a 2-deep one (11008 x 4096: 8.4 -> 7.8 us)
+    if (s.K <= 4096) return f8_skinny_flags<16, 3>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+    return f8_skinny_flags<16, 2>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
+  }
+  if (M <= 4 && T <= 1024)  // four waves, activation tiles through LDS (4096 x 12288, M = 4: 9.8 -> 9.2 us)
+    return f8_skinny_flags<4, 4, true>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
   if (M <= 16 && T <= 256 && s.K <= 4096)
     return f8_skinny_flags<16, 3, true>(s, M, xq, rs, xscale, tiled_w, tiled_s, tiled_z, bias, y, st);
   if (M <= 16 && T <= 1024)
