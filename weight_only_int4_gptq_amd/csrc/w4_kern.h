@@ -922,20 +922,37 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
 
 // y[m][n] = round(sum_z part[z][m][n] + bias[n]) for split-K launches; four
 // consecutive columns per thread (N is a multiple of 16).
-template <bool BF16>
+// SPLITS: the number of partial planes when known at compile time (all
+// loads of an element are then in flight together); 0 reads `splits`.
+template <bool BF16, int SPLITS>
 __global__ void split_reduce(const float* __restrict__ part, const uint16_t* __restrict__ bias,
                              uint16_t* __restrict__ y, int64_t M, int64_t N, int splits) {
   const int64_t total4 = M * N / 4, plane4 = total4;
   const float4* p4 = reinterpret_cast<const float4*>(part);
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total4;
        idx += (int64_t)gridDim.x * blockDim.x) {
-    float4 a = p4[idx];
-    for (int z = 1; z < splits; ++z) {
-      const float4 b = p4[z * plane4 + idx];
-      a.x += b.x;
-      a.y += b.y;
-      a.z += b.z;
-      a.w += b.w;
+    float4 a;
+    if constexpr (SPLITS > 0) {
+      float4 v[SPLITS];
+#pragma unroll
+      for (int z = 0; z < SPLITS; ++z) v[z] = p4[z * plane4 + idx];
+      a = v[0];
+#pragma unroll
+      for (int z = 1; z < SPLITS; ++z) {
+        a.x += v[z].x;
+        a.y += v[z].y;
+        a.z += v[z].z;
+        a.w += v[z].w;
+      }
+    } else {
+      a = p4[idx];
+      for (int z = 1; z < splits; ++z) {
+        const float4 b = p4[z * plane4 + idx];
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+      }
     }
     const int64_t n = (idx * 4) % N;
     if (bias != nullptr) {
@@ -1151,7 +1168,12 @@ hipError_t run_wide(const Args& a, const uint16_t* x, hipStream_t st) {
   const int64_t total4 = a.M * a.N / 4;
   int64_t blocks = (total4 + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  split_reduce<BF16><<<(unsigned)blocks, 256, 0, st>>>(a.part, a.bias, a.y, a.M, a.N, splits);
+  switch (splits) {
+    case 2: split_reduce<BF16, 2><<<(unsigned)blocks, 256, 0, st>>>(a.part, a.bias, a.y, a.M, a.N, splits); break;
+    case 4: split_reduce<BF16, 4><<<(unsigned)blocks, 256, 0, st>>>(a.part, a.bias, a.y, a.M, a.N, splits); break;
+    case 8: split_reduce<BF16, 8><<<(unsigned)blocks, 256, 0, st>>>(a.part, a.bias, a.y, a.M, a.N, splits); break;
+    default: split_reduce<BF16, 0><<<(unsigned)blocks, 256, 0, st>>>(a.part, a.bias, a.y, a.M, a.N, splits);
+  }
   return hipGetLastError();
 }
 
