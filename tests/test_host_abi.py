@@ -227,8 +227,9 @@ def test_split_k_workspace_is_sized_and_checked(W):
     assert W.w4_workspace_size(L, 128) == 4 * 128 * 8192 * 4
     assert W.w4_workspace_size(L, 1) == 0
     # bf16 from M = 256 (and M = 64 on long or wide layers): the row sums of x
-    # per 128-row block follow, [K / 128][M] fp32
-    assert W.w4_workspace_size(L, 256) == 4 * 256 * 8192 * 4 + 64 * 256 * 4
+    # per 128-row block follow, [K / 128][M] fp32; above 128 rows a K of
+    # 8192 splits two ways
+    assert W.w4_workspace_size(L, 256) == 2 * 256 * 8192 * 4 + 64 * 256 * 4
     assert W.w4_workspace_size(L, 2048) == 64 * 2048 * 4
     # a longer K splits eight ways (four at M = 256)
     L2 = W.make_layer(28672, 8192, 128, False, False, "bf16")
