@@ -702,8 +702,10 @@ MOE_VARIANTS = [
     ("std-bf16-g64-sym", "std", 64, False, "bf16", False),
     ("std-fp16-g32-z", "std", 32, True, "fp16", False),
 ]
-# rows per expert: empty experts, 1-row experts, ragged tiles, up to 130 rows
-MOE_ROWS = [[3, 0, 17, 1, 40, 0], [16, 16, 16, 16], [130, 0, 64, 33], [1, 1, 1, 1, 1, 1, 1, 1]]
+# rows per expert: empty experts, 1-row experts, ragged tiles, up to 300 rows
+# (fp16 experts of >= 128 rows take the 128 x 256 tile kernel)
+MOE_ROWS = [[3, 0, 17, 1, 40, 0], [16, 16, 16, 16], [130, 0, 64, 33], [1, 1, 1, 1, 1, 1, 1, 1],
+            [300, 0, 5, 140]]
 
 
 @pytest.mark.parametrize("v", MOE_VARIANTS, ids=[v[0] for v in MOE_VARIANTS])
@@ -732,7 +734,7 @@ def test_moe_linear_matches_the_oracle(W, v):
             ref = O.reference_moe(x, offsets, fmt, dtype, experts, gs, bias=bias)
             # max_rows sizes the launch only: estimates below the largest
             # expert (1, 17) must still compute every row
-            for max_rows in (0, max(rows), 1, 17):
+            for max_rows in (0, max(rows), 1, 17, 128):
                 say(f"moe {name} N={N} rows={rows} max_rows={max_rows}")
                 buf = filled((R + 2, N), act_dtype(dtype), 0x7F)
                 moe.apply(to_dev(x), to_dev(offsets), max_rows, to_dev(bias) if bias is not None else None,

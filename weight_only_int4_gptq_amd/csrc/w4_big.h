@@ -85,15 +85,20 @@ __device__ __forceinline__ void big_tile_of(int64_t L, int64_t tiles_m, int64_t 
   tn = in / rows;
 }
 
-template <int WM, int WN, int MT, int NT, int S, int GM, bool HAS_Z>
-__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __restrict__ x,
-                                                             const u4* __restrict__ qw,
-                                                             const uint16_t* __restrict__ sc,
-                                                             const uint32_t* __restrict__ zs,
-                                                             const uint16_t* __restrict__ bias,
-                                                             uint16_t* __restrict__ y, int64_t M, int64_t K,
+// GROUPED: a mixture-of-experts launch, grid (column tiles, row tiles,
+// experts); expert e owns rows [offs[e], offs[e + 1]) of x and y (clamped
+// into the M rows given) and the e-th copy of the tiled weights, scales,
+// zeros and bias, each following the previous expert's.
+template <int WM, int WN, int MT, int NT, int S, int GM, bool HAS_Z, bool GROUPED = false>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __restrict__ x_in,
+                                                             const u4* __restrict__ qw_in,
+                                                             const uint16_t* __restrict__ sc_in,
+                                                             const uint32_t* __restrict__ zs_in,
+                                                             const uint16_t* __restrict__ bias_in,
+                                                             uint16_t* __restrict__ y_in, int64_t M_in, int64_t K,
                                                              int64_t N, int G,
-                                                             int64_t tiles_m, int64_t tiles_n, int64_t group_m) {
+                                                             int64_t tiles_m, int64_t tiles_n, int64_t group_m,
+                                                             const int32_t* __restrict__ offs) {
   using C = BigCfg<WM, WN, MT, NT, S>;
   constexpr int NP = Groups<GM>::kPeriods;  // scale periods per 128-row block
   constexpr int SPP = 8 / NP;               // 16-deep steps per period
@@ -121,11 +126,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
   const int64_t nblk = K / kTileK;
   constexpr int64_t kb0 = 0;  // the whole of K (the issue and pipeline code count blocks from kb0)
   const int64_t nb = nblk;
-  int64_t tm, tn;
-  big_tile_of(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
-  const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
   const uint32_t zshift = 4u * (uint32_t)(c & 7);
   const NibbleMasks nm = NibbleMasks::make();
+
+  // one 32 MT WM x 32 NT WN output tile at (m0, n0) of an M-row problem
+  auto tile = [&](const int64_t m0, const int64_t n0, const uint16_t* __restrict__ x, const u4* __restrict__ qw,
+                  const uint16_t* __restrict__ sc, const uint32_t* __restrict__ zs,
+                  const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, const int64_t M)
+                  __attribute__((always_inline)) {
 
   // weights, scales, zeros of the lane's column in each 32-column tile
   // (strips past the end read strip 0 and are never stored)
@@ -278,6 +286,38 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
         y[m * N + n] = f32_to_act<false>(acc[i][nt][r] * s_prev[nt] + bv);
       }
   }
+  };
+
+  if constexpr (GROUPED) {
+    const int64_t e = blockIdx.z;
+    int64_t r0 = offs[e], r1 = offs[e + 1];
+    r0 = r0 < 0 ? 0 : (r0 > M_in ? M_in : r0);
+    r1 = r1 < r0 ? r0 : (r1 > M_in ? M_in : r1);
+    const int64_t Me = r1 - r0;
+    const u4* qwe = qw_in + e * (K * T * kTileN / 32);
+    const uint16_t* sce = sc_in + e * T * kTileN * G;
+    const uint32_t* zse = HAS_Z ? zs_in + e * T * 2 * G : zs_in;
+    const uint16_t* biase = bias_in != nullptr ? bias_in + e * N : nullptr;
+    // every row tile of the expert, in steps of gridDim.y (an expert with
+    // more rows than the launch height is still computed whole); the weight
+    // bases pass through an opaque zero made inside the loop so that the
+    // compiler cannot hoist the prologue's weight loads out of it (the
+    // counted vmcnt waits assume the issue order)
+    for (int64_t m0 = (int64_t)blockIdx.y * C::BM; m0 < Me; m0 += (int64_t)gridDim.y * C::BM) {
+      int64_t z0;
+      asm volatile("s_mov_b64 %0, 0" : "=s"(z0));
+      tile(m0, (int64_t)blockIdx.x * C::BN, x_in + r0 * K, qwe + z0, sce + z0, zse + z0, biase, y_in + r0 * N, Me);
+      // the clamped prefetches of the last blocks may still be landing in
+      // the LDS slots: drain them, and let every wave finish with the slots,
+      // before the next row tile's prologue refills them
+      wait_vmcnt<0>();
+      lds_barrier();
+    }
+  } else {
+    int64_t tm, tn;
+    big_tile_of(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    tile(tm * C::BM, tn * C::BN, x_in, qw_in, sc_in, zs_in, bias_in, y_in, M_in);
+  }
 }
 
 // Launch of one configuration (fp16 only, the whole of K per workgroup);
@@ -289,7 +329,24 @@ hipError_t run_big(const Args& a, const uint16_t* x, int64_t group_m, hipStream_
   const int64_t tiles_m = (a.M + C::BM - 1) / C::BM, tiles_n = (Np + C::BN - 1) / C::BN;
   if (tiles_m * tiles_n > 0x7FFFFFFF || group_m < 1) return hipErrorInvalidValue;
   gemm_big<WM, WN, MT, NT, S, GM, HZ><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
-      x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N, a.G, tiles_m, tiles_n, group_m);
+      x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N, a.G, tiles_m, tiles_n, group_m, nullptr);
+  return hipGetLastError();
+}
+
+// Grouped launch: a.offs [a.groups + 1] expert row offsets, a.max_rows the
+// most rows any expert has (the launch height; a larger expert is still
+// computed whole).
+template <int WM, int WN, int MT, int NT, int S, int GM, bool HZ>
+hipError_t run_big_grouped(const Args& a, hipStream_t st) {
+  using C = BigCfg<WM, WN, MT, NT, S>;
+  const int64_t Np = (a.N + kTileN - 1) / kTileN * kTileN;
+  const int64_t tiles_n = (Np + C::BN - 1) / C::BN, tiles_m = (a.max_rows + C::BM - 1) / C::BM;
+  if (a.offs == nullptr || a.groups < 1 || a.groups > 65535 || tiles_m < 1 || tiles_m > 65535 ||
+      tiles_n > 0x7FFFFFFF)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles_n, (unsigned)tiles_m, (unsigned)a.groups);
+  gemm_big<WM, WN, MT, NT, S, GM, HZ, true><<<grid, 64 * WM * WN, 0, st>>>(
+      a.x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N, a.G, tiles_m, tiles_n, 1, a.offs);
   return hipGetLastError();
 }
 

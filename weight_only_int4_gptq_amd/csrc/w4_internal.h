@@ -98,6 +98,10 @@ int64_t big_tile_cols();
 int big_threads();
 hipError_t launch_big(const Shape& s, int64_t M, const uint16_t* x, const int32_t* tiled_w, const void* tiled_s,
                       const int32_t* tiled_z, const void* bias, void* y, hipStream_t st);
+// grouped (mixture-of-experts) launch of the same kernel, fp16 only
+hipError_t launch_big_moe(const Shape& s, int experts, int64_t total_rows, int64_t max_rows, const void* x,
+                          const int32_t* offsets, const int32_t* tiled_w, const void* tiled_s,
+                          const int32_t* tiled_z, const void* bias, void* y, hipStream_t st);
 
 // ---- INT4 weights x FP8 activations (w4_fp8.hip); the GEMM takes the padded shape ----
 size_t f8_rows(int64_t M);  // rows of the row-sum array (M rounded up to 4)

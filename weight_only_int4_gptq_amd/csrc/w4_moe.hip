@@ -4,6 +4,8 @@
 
 namespace w4 {
 
+constexpr int64_t kMoeBigRows = 128;
+
 GemmPlan plan_moe(const Shape& s, int64_t max_rows, int experts) {
   // grouped launch of the wide kernel (no split-K): 16-row tiles for up to
   // 16 rows per expert (two waves of one strip each once there are >= 1024
@@ -11,6 +13,11 @@ GemmPlan plan_moe(const Shape& s, int64_t max_rows, int experts) {
   // tile not taller than the rows that still gives >= 256 workgroups over
   // all experts
   const int64_t T = s.Np / kTileN;
+  if (!s.bf16 && max_rows >= kMoeBigRows) {
+    // fp16 experts of at least kMoeBigRows rows: 128 x 256 tiles of 32x32x16
+    // MFMAs, as for large-M fp16 layers
+    return GemmPlan{GemmKind::kBig, 0, 0, 0, false, "w4_big_128x256_grouped"};
+  }
   int idx = kNumWide - 1;
   if (max_rows <= 16) {
     idx = T * experts >= 1024 ? kWide16x32w2 : kWide16x16;
@@ -53,6 +60,8 @@ hipError_t launch_moe(const Shape& s, int experts, int64_t total_rows, int64_t m
   a.G = s.G;
   a.gs = s.gs;
   const GemmPlan p = plan_moe(s, max_rows, experts);
+  if (p.kind == GemmKind::kBig)
+    return launch_big_moe(s, experts, total_rows, max_rows, x, offsets, tiled_w, tiled_s, tiled_z, bias, y, st);
   return wide_dispatch<true>(p.wide, s, a, a.x, st);
 }
 
