@@ -135,29 +135,38 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
                   const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, const int64_t M)
                   __attribute__((always_inline)) {
 
-  // weights, scales, zeros of the lane's column in each 32-column tile
-  // (strips past the end read strip 0 and are never stored)
-  const u4* wp[NT];
-  const uint16_t* sp[NT];
-  const uint32_t* zp[NT];
+  // Operand addresses: a uniform base per 32-column tile (and per row tile
+  // for the activations) plus a 32-bit per-lane byte offset, so the loads
+  // take the scalar-base + vector-offset form and the lanes hold one
+  // register per address instead of two.  Weights, scales and zeros of the
+  // lane's column: a strip past the end reads the tile's first strip, a
+  // tile past the end strip 0 (neither is stored).
+  const char* wb[NT];
+  const char* sb[NT];
+  const char* zb[NT];
+  uint32_t wo[NT], so[NT], zo[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int64_t t = (n0 + (int64_t)(wn * NT + nt) * 32) / kTileN + (c >> 4);
-    const int64_t tt = t < T ? t : 0;
-    wp[nt] = qw + tt * nblk * 64 + (c & 15) + 16 * h;
-    sp[nt] = sc + tt * G * kTileN + (c & 15);
-    zp[nt] = HAS_Z ? zs + tt * G * 2 + ((c & 15) >> 3) : nullptr;
+    const int64_t t0 = (n0 + (int64_t)(wn * NT + nt) * 32) / kTileN;  // uniform
+    const int64_t tb = t0 < T ? t0 : 0;
+    const uint32_t ls = t0 + (c >> 4) < T ? (uint32_t)(c >> 4) : 0u;  // lane's strip within the tile
+    wb[nt] = reinterpret_cast<const char*>(qw + tb * nblk * 64);
+    sb[nt] = reinterpret_cast<const char*>(sc + tb * G * kTileN);
+    zb[nt] = reinterpret_cast<const char*>(HAS_Z ? zs + tb * G * 2 : zs);
+    wo[nt] = (uint32_t)((ls * nblk * 64 + (c & 15) + 16 * h) * sizeof(u4));
+    so[nt] = (uint32_t)((ls * G * kTileN + (c & 15)) * sizeof(uint16_t));
+    zo[nt] = (uint32_t)((ls * G * 2 + ((c & 15) >> 3)) * sizeof(uint32_t));
   }
   // staging: load i of this wave fills rows 4 (NA wave + i) .. + 3 of the
   // tile; lane l lands at chunk position l % 16 of row base + l / 16 and so
   // loads logical chunk (l % 16) ^ (row % 16)
-  const uint16_t* ap[NA];
+  const char* ab = reinterpret_cast<const char*>(x + m0 * K);
+  uint32_t ao[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int row = 4 * (NA * wave + i) + (lane >> 4);
-    int64_t m = m0 + row;
-    m = m < M ? m : M - 1;
-    ap[i] = x + m * K + 8 * ((lane & 15) ^ (row & 15));
+    const int64_t r = m0 + row < M ? row : M - 1 - m0;
+    ao[i] = (uint32_t)((r * K + 8 * ((lane & 15) ^ (row & 15))) * sizeof(uint16_t));
   }
 
   struct Slot {
@@ -172,17 +181,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const int64_t g = Groups<GM>::group((int)b, p);
-        r.s[nt][p] = sp[nt][g * kTileN];
-        r.z[nt][p] = HAS_Z ? zp[nt][g * 2] : 0u;
+        const uint32_t g = (uint32_t)Groups<GM>::group((int)b, p);
+        r.s[nt][p] = *reinterpret_cast<const uint16_t*>(sb[nt] + (so[nt] + g * (uint32_t)(kTileN * sizeof(uint16_t))));
+        r.z[nt][p] = HAS_Z ? *reinterpret_cast<const uint32_t*>(zb[nt] + (zo[nt] + g * 8u)) : 0u;
       }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      r.w[nt][0] = wp[nt][b * 64];
-      r.w[nt][1] = wp[nt][b * 64 + 32];
+      const uint32_t bo = wo[nt] + (uint32_t)b * 1024u;
+      r.w[nt][0] = *reinterpret_cast<const u4*>(wb[nt] + bo);
+      r.w[nt][1] = *reinterpret_cast<const u4*>(wb[nt] + (bo + 512u));
     }
 #pragma unroll
-    for (int i = 0; i < NA; ++i) load_lds16(ap[i] + b * kTileK, slot_lds(slot) + 4 * (NA * wave + i) * kTileK);
+    for (int i = 0; i < NA; ++i)
+      load_lds16(reinterpret_cast<const uint16_t*>(ab + (ao[i] + (uint32_t)b * (uint32_t)(kTileK * sizeof(uint16_t)))),
+                 slot_lds(slot) + 4 * (NA * wave + i) * kTileK);
   };
 
   f16v acc[MT][NT];
