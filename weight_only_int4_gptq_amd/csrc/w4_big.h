@@ -217,6 +217,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
   auto compute = [&](const Slot& r, int slot) __attribute__((always_inline)) {
     // row of this lane in row tile i: 32 (MT wm + i) + c, so row % 16 == c % 16
     const uint16_t* xa = slot_lds(slot) + (wm * MT * 32 + c) * kTileK;
+    // A operands double-buffered: step s + 1's LDS reads are issued at the
+    // start of step s (the scheduling barrier keeps the compiler from
+    // sinking them back to just before their first use), so their latency
+    // is covered by a whole step of MFMAs
+    u4 abuf[2][MT];
+    auto read_a = [&](int step, u4 (&dst)[MT]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        dst[i] = *reinterpret_cast<const u4*>(xa + i * 32 * kTileK + 8 * ((2 * step + h) ^ (c & 15)));
+    };
+    read_a(0, abuf[0]);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       uint32_t n1[NT], n2[NT];
@@ -233,10 +244,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
 #pragma unroll
       for (int st = 0; st < SPP; ++st) {
         const int step = p * SPP + st;  // 16-deep step of the block, 0..7
-        u4 a[MT];
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-          a[i] = *reinterpret_cast<const u4*>(xa + i * 32 * kTileK + 8 * ((2 * step + h) ^ (c & 15)));
+        if (step + 1 < 8) read_a(step + 1, abuf[(step + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const u4(&a)[MT] = abuf[step & 1];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const uint32_t w = r.w[nt][step & 1][step >> 1];
