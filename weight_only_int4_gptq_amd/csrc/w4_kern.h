@@ -706,28 +706,33 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
   // zero bases)
   auto tile = [&](const int64_t m0, const u4* qwb, const uint16_t* scb, const uint32_t* zsb)
                   __attribute__((always_inline)) {
-  // per-strip operand pointers (strips past the end read strip 0)
-  const u4* wp[NS];
-  const uint16_t* sp[NS];
-  const uint32_t* zp[NS];
+  // Operand addresses: a uniform base per strip (and per row tile for the
+  // activations) plus a 32-bit per-lane byte offset, so the loads take the
+  // scalar-base + vector-offset form.  Strips past the end read strip 0.
+  const char* wb[NS];
+  const char* sb[NS];
+  const char* zb[NS];
 #pragma unroll
   for (int nt = 0; nt < NS; ++nt) {
     const int64_t t = tw0 + nt;
     const int64_t tt = t < T ? t : 0;
-    wp[nt] = qwb + tt * nblk * 64 + lane;
-    sp[nt] = scb + tt * G * kTileN + c;
-    zp[nt] = HAS_Z ? zsb + tt * G * 2 + (c >> 3) : nullptr;
+    wb[nt] = reinterpret_cast<const char*>(qwb + tt * nblk * 64);
+    sb[nt] = reinterpret_cast<const char*>(scb + tt * G * kTileN);
+    zb[nt] = reinterpret_cast<const char*>(HAS_Z ? zsb + tt * G * 2 : zsb);
   }
+  const uint32_t wo = (uint32_t)lane * (uint32_t)sizeof(u4);
+  const uint32_t so = (uint32_t)c * (uint32_t)sizeof(uint16_t);
+  const uint32_t zo = (uint32_t)(c >> 3) * (uint32_t)sizeof(uint32_t);
   // staging: load i of this wave fills rows 4 (NA wave + i) .. + 3 of the
   // tile; lane l lands at chunk position l % 16 of row base + l / 16 and so
   // loads logical chunk (l % 16) ^ (row % 16)
-  const uint16_t* ap[NA];
+  const char* ab = reinterpret_cast<const char*>(x + m0 * K);
+  uint32_t ao[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int row = 4 * (NA * wave + i) + quad;
-    int64_t m = m0 + row;
-    m = m < M ? m : M - 1;
-    ap[i] = x + m * K + 8 * (c ^ (row & 15));
+    const int64_t r = m0 + row < M ? row : M - 1 - m0;
+    ao[i] = (uint32_t)((r * K + 8 * (c ^ (row & 15))) * sizeof(uint16_t));
   }
 
   struct Slot {
@@ -742,14 +747,16 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_wide(const uint16_t* __restri
     for (int nt = 0; nt < NS; ++nt)
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const int64_t g = Groups<GM>::group((int)b, p);
-        r.s[nt][p] = sp[nt][g * kTileN];
-        r.z[nt][p] = HAS_Z ? zp[nt][g * 2] : 0u;
+        const uint32_t g = (uint32_t)Groups<GM>::group((int)b, p);
+        r.s[nt][p] = *reinterpret_cast<const uint16_t*>(sb[nt] + (so + g * (uint32_t)(kTileN * sizeof(uint16_t))));
+        r.z[nt][p] = HAS_Z ? *reinterpret_cast<const uint32_t*>(zb[nt] + (zo + g * 8u)) : 0u;
       }
 #pragma unroll
-    for (int nt = 0; nt < NS; ++nt) r.w[nt] = wp[nt][b * 64];
+    for (int nt = 0; nt < NS; ++nt) r.w[nt] = *reinterpret_cast<const u4*>(wb[nt] + (wo + (uint32_t)b * 1024u));
 #pragma unroll
-    for (int i = 0; i < NA; ++i) load_lds16(ap[i] + b * kTileK, slot_lds(slot) + 4 * (NA * wave + i) * kTileK);
+    for (int i = 0; i < NA; ++i)
+      load_lds16(reinterpret_cast<const uint16_t*>(ab + (ao[i] + (uint32_t)b * (uint32_t)(kTileK * sizeof(uint16_t)))),
+                 slot_lds(slot) + 4 * (NA * wave + i) * kTileK);
     if constexpr (RSIN) {
       // lane l of load (p, h): the sum of row m0 + 64 h + l over period
       // b NP + p (rows past M read row M - 1; never used)
