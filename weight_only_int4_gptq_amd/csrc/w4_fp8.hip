@@ -171,36 +171,42 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_f8(const uint8_t* __restrict_
   const int64_t tw0 = ((int64_t)blockIdx.x * WN + wave) * NS;
   const uint32_t zshift = 4u * (uint32_t)(c & 7);
 
-  const u4* wp[NS];
-  const uint16_t* sp[NS];
-  const uint32_t* zp[NS];
+  // operand addresses: uniform bases (per strip, per row tile) plus 32-bit
+  // per-lane byte offsets, so the loads take the scalar-base form; strips
+  // past the end read strip 0
+  const char* wb[NS];
+  const char* sb[NS];
+  const char* zb[NS];
 #pragma unroll
   for (int nt = 0; nt < NS; ++nt) {
     const int64_t t = tw0 + nt;
     const int64_t tt = t < T ? t : 0;
-    wp[nt] = qw + tt * nblk * 64 + lane;
-    sp[nt] = sc + tt * G * kTileN + c;
-    zp[nt] = HAS_Z ? zs + tt * G * 2 + (c >> 3) : nullptr;
+    wb[nt] = reinterpret_cast<const char*>(qw + tt * nblk * 64);
+    sb[nt] = reinterpret_cast<const char*>(sc + tt * G * kTileN);
+    zb[nt] = reinterpret_cast<const char*>(HAS_Z ? zs + tt * G * 2 : zs);
   }
+  const uint32_t wo = (uint32_t)lane * (uint32_t)sizeof(u4);
+  const uint32_t so = (uint32_t)c * (uint32_t)sizeof(uint16_t);
+  const uint32_t zo = (uint32_t)(c >> 3) * (uint32_t)sizeof(uint32_t);
   // staging: load i of this wave fills rows 8 (NA wave + i) .. + 7; lane l
   // lands at position l % 8 of row base + l / 8 and so loads logical chunk
   // (l % 8) ^ swz(row)
-  const uint8_t* ap[NA];
+  const char* ab = reinterpret_cast<const char*>(xq + m0 * K);
+  uint32_t ao[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int row = 8 * (NA * wave + i) + (lane >> 3);
-    int64_t m = m0 + row;
-    m = m < M ? m : M - 1;
-    ap[i] = xq + m * K + 16 * ((lane & 7) ^ swz8(row));
+    const int64_t r = m0 + row < M ? row : M - 1 - m0;
+    ao[i] = (uint32_t)(r * K + 16 * ((lane & 7) ^ swz8(row)));
   }
   // the lane's four output rows of tile i: 16 i + 4 quad + 0..3 (their block
   // sums are one 16-byte load; groups of rows past Mr, never stored, read
   // the last group)
-  const float* rp[MT];
+  uint32_t ro[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     const int64_t r = m0 + 16 * i + 4 * quad;
-    rp[i] = rs + (r < Mr ? r : Mr - 4);
+    ro[i] = (uint32_t)((r < Mr ? r : Mr - 4) * sizeof(float));
   }
 
   struct Slot {
@@ -212,19 +218,19 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_f8(const uint8_t* __restrict_
   Slot rg[S];
 
   auto issue = [&](int64_t b, Slot& r, int slot) __attribute__((always_inline)) {
-    const int64_t g = PERCH ? 0 : b;
+    const uint32_t g = PERCH ? 0u : (uint32_t)b;
 #pragma unroll
     for (int nt = 0; nt < NS; ++nt) {
-      r.s[nt] = sp[nt][g * kTileN];
-      r.z[nt] = HAS_Z ? zp[nt][g * 2] : 0u;
+      r.s[nt] = *reinterpret_cast<const uint16_t*>(sb[nt] + (so + g * (uint32_t)(kTileN * sizeof(uint16_t))));
+      r.z[nt] = HAS_Z ? *reinterpret_cast<const uint32_t*>(zb[nt] + (zo + g * 8u)) : 0u;
     }
 #pragma unroll
-    for (int i = 0; i < MT; ++i) r.rsum[i] = *reinterpret_cast<const f4*>(rp[i] + b * Mr);
+    for (int i = 0; i < MT; ++i) r.rsum[i] = *reinterpret_cast<const f4*>(reinterpret_cast<const char*>(rs + b * Mr) + ro[i]);
 #pragma unroll
-    for (int nt = 0; nt < NS; ++nt) r.w[nt] = wp[nt][b * 64];
+    for (int nt = 0; nt < NS; ++nt) r.w[nt] = *reinterpret_cast<const u4*>(wb[nt] + (wo + (uint32_t)b * 1024u));
 #pragma unroll
     for (int i = 0; i < NA; ++i)
-      load_lds16(reinterpret_cast<const uint16_t*>(ap[i] + b * 128),
+      load_lds16(reinterpret_cast<const uint16_t*>(ab + (ao[i] + (uint32_t)b * 128u)),
                  reinterpret_cast<uint16_t*>(slot_lds(slot) + 8 * (NA * wave + i) * 128));
   };
 
@@ -312,8 +318,8 @@ __global__ __launch_bounds__(64 * WN, 1) void gemm_f8(const uint8_t* __restrict_
     const float bv = bias != nullptr ? act_to_f32<BF16>(bias[n]) : 0.f;
     float s_ch = 1.f, z_ch = 0.f;
     if constexpr (PERCH) {
-      s_ch = act_to_f32<BF16>(sp[nt][0]);
-      z_ch = HAS_Z ? (float)((zp[nt][0] >> zshift) & 0xFu) : 8.f;
+      s_ch = act_to_f32<BF16>(*reinterpret_cast<const uint16_t*>(sb[nt] + so));
+      z_ch = HAS_Z ? (float)((*reinterpret_cast<const uint32_t*>(zb[nt] + zo) >> zshift) & 0xFu) : 8.f;
     }
 #pragma unroll
     for (int i = 0; i < MT; ++i)
