@@ -270,11 +270,15 @@ struct BlockRegs {
 template <int MT, int NB, int GM, bool HAS_Z, bool XL>
 struct LaneView {
   static constexpr int NP = Groups<GM>::kPeriods;
-  const u4* w[NB];            // tiled words of strip s at block 0 (lane's 16 bytes)
-  const uint16_t* sc[NB];     // scale of column c of strip s, group 0
-  const uint32_t* zs[NB];     // zero word holding column c of strip s, group 0
-  const uint16_t* xr[MT];     // x row of tile i + 8 * quad
-  const uint16_t* xd[4];      // AD: source of this lane's 16 bytes in direct-to-LDS load i of a block
+  // Addresses as a uniform base (per strip, per row tile) plus a 32-bit
+  // per-lane byte offset, so the loads take the scalar-base form.
+  const char* wb[NB];         // tiled words of strip s at block 0
+  const char* sb[NB];         // scales of strip s, group 0
+  const char* zb[NB];         // zero words of strip s, group 0
+  const char* xb;             // x row m0
+  uint32_t wo, so, zo;        // lane's 16 bytes of a block, its column's scale and zero word
+  uint32_t xo[MT];            // x row of tile i + 8 * quad, relative to xb
+  uint32_t xdo[4];            // AD: source of this lane's 16 bytes in direct-to-LDS load i of a block
   const uint16_t* xl;         // XL: LDS row of this lane + 8 * quad
   bool row_ok[MT];            // row of tile i is < M
   int64_t nblk;
@@ -286,16 +290,20 @@ struct LaneView {
     nblk = K / kTileK;
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
-      w[s] = qw + (t0 + s) * nblk * 64 + lane;
-      sc[s] = scl + (t0 + s) * G * kTileN + c;
-      zs[s] = HAS_Z ? zsp + (t0 + s) * G * 2 + (c >> 3) : nullptr;
+      wb[s] = reinterpret_cast<const char*>(qw + (t0 + s) * nblk * 64);
+      sb[s] = reinterpret_cast<const char*>(scl + (t0 + s) * G * kTileN);
+      zb[s] = reinterpret_cast<const char*>(HAS_Z ? zsp + (t0 + s) * G * 2 : zsp);
     }
+    wo = (uint32_t)lane * (uint32_t)sizeof(u4);
+    so = (uint32_t)c * (uint32_t)sizeof(uint16_t);
+    zo = (uint32_t)(c >> 3) * (uint32_t)sizeof(uint32_t);
+    xb = reinterpret_cast<const char*>(x + m0 * K);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       int64_t m = m0 + 16 * i + c;
       row_ok[i] = m < M;
       m = m < M ? m : M - 1;
-      xr[i] = x + m * K + 8 * quad;
+      xo[i] = (uint32_t)(((m - m0) * K + 8 * quad) * (int64_t)sizeof(uint16_t));
     }
     // LDS rows >= M are never staged; read row 0 instead
     xl = xlds + (row_ok[0] ? c : 0) * (K + kXPad) + 8 * quad;
@@ -308,7 +316,7 @@ struct LaneView {
       const int row = 4 * i + quad;
       int64_t m = m0 + row;
       m = m < M ? m : M - 1;
-      xd[i] = x + m * K + 8 * (c ^ row);
+      xdo[i] = (uint32_t)(((m - m0) * K + 8 * (c ^ row)) * (int64_t)sizeof(uint16_t));
     }
   }
 
@@ -318,16 +326,18 @@ struct LaneView {
   template <int AR>
   __device__ __forceinline__ void load_a_dma(int kb, uint16_t* dst) const {
 #pragma unroll
-    for (int i = 0; i < AR / 4; ++i) load_lds16(xd[i] + (int64_t)kb * kTileK, dst + 4 * i * kTileK);
+    for (int i = 0; i < AR / 4; ++i)
+      load_lds16(reinterpret_cast<const uint16_t*>(xb + (xdo[i] + (uint32_t)kb * (uint32_t)(kTileK * sizeof(uint16_t)))),
+                 dst + 4 * i * kTileK);
   }
 
   // A operands of block kb straight from global memory.
   __device__ __forceinline__ void load_a_global(int kb, u4 (&a)[MT][4]) const {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int k = kb * kTileK + 32 * j;
+      const uint32_t k = ((uint32_t)kb * kTileK + 32u * j) * (uint32_t)sizeof(uint16_t);
 #pragma unroll
-      for (int i = 0; i < MT; ++i) a[i][j] = *reinterpret_cast<const u4*>(xr[i] + k);
+      for (int i = 0; i < MT; ++i) a[i][j] = *reinterpret_cast<const u4*>(xb + (xo[i] + k));
     }
   }
 
@@ -342,12 +352,12 @@ struct LaneView {
   __device__ __forceinline__ void load_block(int b, BlockRegs<MT, NB, NP, NOA>& r) const {
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
-      r.wv[s] = w[s][(int64_t)b * 64];
+      r.wv[s] = *reinterpret_cast<const u4*>(wb[s] + (wo + (uint32_t)b * 1024u));
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const int g = Groups<GM>::group(b, p);
-        r.sraw[s][p] = sc[s][(int64_t)g * kTileN];
-        r.zraw[s][p] = HAS_Z ? zs[s][(int64_t)g * 2] : 0u;
+        const uint32_t g = (uint32_t)Groups<GM>::group(b, p);
+        r.sraw[s][p] = *reinterpret_cast<const uint16_t*>(sb[s] + (so + g * (uint32_t)(kTileN * sizeof(uint16_t))));
+        r.zraw[s][p] = HAS_Z ? *reinterpret_cast<const uint32_t*>(zb[s] + (zo + g * 8u)) : 0u;
       }
     }
     if constexpr (!NOA) load_a_global(b, r.a);
