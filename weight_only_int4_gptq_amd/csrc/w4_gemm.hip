@@ -124,11 +124,12 @@ GemmPlan plan_tiles(const Shape& s, int64_t M) {
     // there: loading them into registers touches 16 half-used cache lines per
     // load, which measured 12-19% slower at M = 16 on the narrow layers
     // (11008 x 4096: 13.6 -> 11.0 us; 4096 x 4096: 6.6 -> 5.8 us) and 15% at
-    // 8192 x 8192.  Eight waves; the ring and the reduction take one CU's
-    // LDS, so the strips per workgroup keep the grid to one round of at most
-    // 256 workgroups: one strip (ring 2) up to 256 strips, two (ring 3) up
-    // to 512, three (ring 3) up to 768 (12288: 10.9 -> 10.3 us against the
-    // shared-tile kernel above; 9216: 13.7 -> 9.5 us against two strips)
+    // 8192 x 8192.  Eight waves with a 3-deep ring (11008 x 4096: 11.3 ->
+    // 10.9 us against 2-deep); the ring and the reduction take one CU's LDS,
+    // so the strips per workgroup keep the grid to one round of at most 256
+    // workgroups: one strip up to 256 strips, two up to 512, three up to 768
+    // (12288: 10.9 -> 10.3 us against the shared-tile kernel above; 9216:
+    // 13.7 -> 9.5 us against two strips)
     if (T <= 256)
       p = GemmPlan{GemmKind::kSkinny, 1, 1, 8, false, "w4_skinny_dma_k8"};
     else if (T <= 512)
@@ -290,7 +291,7 @@ hipError_t launch_gemm(const Shape& s0, int64_t M, const void* x, const int32_t*
   if (p.ar == 4) return pick_flags<1, 1, 16, false, 4, 3>(sk, a, st);
   if (p.ar == 16) {
     if (p.nb == 3) return pick_flags<1, 3, 8, false, 16, 3>(sk, a, st);
-    return p.nb == 2 ? pick_flags<1, 2, 8, false, 16, 3>(sk, a, st) : pick_flags<1, 1, 8, false, 16, 2>(sk, a, st);
+    return p.nb == 2 ? pick_flags<1, 2, 8, false, 16, 3>(sk, a, st) : pick_flags<1, 1, 8, false, 16, 3>(sk, a, st);
   }
   if (p.xl) return pick_flags<1, 1, 8, true>(sk, a, st);
   if (p.nb == 2) return p.kw == 16 ? pick_flags<1, 2, 16, false>(sk, a, st) : pick_flags<1, 2, 8, false>(sk, a, st);
