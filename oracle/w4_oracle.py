@@ -23,7 +23,7 @@ Sources (four web pages on vLLM / SGLang quantization):
 * [P4] SGLang quantization design: section 1 (create_weights /
   process_weights_after_loading / apply split).
 
-Readings where the pages leave a point open (each also listed in the design doc):
+Readings where the pages leave a point open:
 
 * AWQ order direction: logical column j of an AWQ word sits in nibble slot
   R[j], R = [0,4,1,5,2,6,3,7] (the constant is used to build the unpack
@@ -35,8 +35,8 @@ Readings where the pages leave a point open (each also listed in the design doc):
 * Zero points are used as stored, for AWQ and standard alike (no +-1).
 * Without zero points the zero is 8 (symmetric 4-bit).
 * A g_idx group index replaces k // group_size.
-* The gfx950 tile layout (``tile_layout``) is this library's own format; it
-  is defined in the design doc and restated in that function's docstring.
+* The gfx950 tile layout (``tile_layout``) is this library's own format,
+  defined in that function's docstring.
 
 Every function below is pinned by ``tests/test_oracle_pins.py``.
 """

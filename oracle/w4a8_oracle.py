@@ -13,7 +13,7 @@ Sources:
   scale per group of 128 elements, fp8 activations quantized with a static
   input scale (per-expert input scales reduced to one scalar by their max).
 
-Readings (each also listed in the design doc):
+Readings:
 
 * FP8 format: E4M3 with no infinities ("fn"), the float8_e4m3fn the
   loading page names: sign bit, four exponent bits (bias 7), three mantissa

@@ -25,6 +25,7 @@ from .gen import (  # noqa: F401
     CONFIGS,
     ConfigCase,
     config_cases,
+    workload_case,
     make_layer_inputs,
     make_acts,
 )

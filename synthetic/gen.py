@@ -134,6 +134,11 @@ def config_cases(cfg_id: int):
     return [c for c in CONFIGS if c.cfg_id == cfg_id]
 
 
+def workload_case(name: str) -> ConfigCase:
+    """The first case of the workload called `name` ("tiny", "decode", ...)."""
+    return next(c for c in CONFIGS if c.name == name)
+
+
 def make_layer_inputs(c: ConfigCase) -> dict:
     """Weights of one layer, in the checkpoint format the workload names.
 

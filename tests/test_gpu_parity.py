@@ -19,7 +19,7 @@ import pytest
 
 import oracle as O
 from synthetic import (
-    CONFIGS, actorder_gidx, constant_words, make_acts, make_layer_inputs, normal_acts, random_words, seeded,
+    CONFIGS, workload_case, actorder_gidx, constant_words, make_acts, make_layer_inputs, normal_acts, random_words, seeded,
     to_bf16_bits, uniform_scales,
 )
 from tests._gpu import act_dtype, filled, say, to_dev, to_host
@@ -228,7 +228,7 @@ def _assert_close(y_bits, ref, dtype, what):
 
 
 def test_linear_tiny_workload(W):
-    c = CONFIGS[0]
+    c = workload_case("tiny")
     Lw = make_layer_inputs(c)
     Lyr = _prepare(W, "awq", c.K, c.N, c.group_size, True, False, "fp16", Lw["qweight"], Lw["qzeros"],
                    Lw["scales"], None)
@@ -401,7 +401,7 @@ def test_linear_zero_scales_give_bias(W):
 def test_linear_m_zero_is_a_no_op(W):
     import torch
     say("M = 0")
-    c = CONFIGS[0]
+    c = workload_case("tiny")
     Lw = make_layer_inputs(c)
     Lyr = _prepare(W, "awq", c.K, c.N, c.group_size, True, False, "fp16", Lw["qweight"], Lw["qzeros"],
                    Lw["scales"], None)
@@ -654,7 +654,7 @@ def test_dequant_dense_exact(W, v):
 def test_dequant_then_matmul_matches_the_oracle(W):
     import torch
     # the unfused path: dense fp16 weight, then the library matmul
-    c = CONFIGS[0]
+    c = workload_case("tiny")
     Lw = make_layer_inputs(c)
     Lyr = _prepare(W, "awq", c.K, c.N, c.group_size, True, False, "fp16", Lw["qweight"], Lw["qzeros"],
                    Lw["scales"], None)
