@@ -693,6 +693,58 @@ def test_linear_smallest_layers(W, dtype):
 
 
 # ----------------------------------------------------------------------------
+# Activations beyond 4 GiB: every kernel addresses its operands as a 64-bit
+# base per row tile plus a 32-bit per-lane offset; rows past the 4 GiB mark
+# (and a ragged last tile) must come out right
+# ----------------------------------------------------------------------------
+
+BIG_X_VARIANTS = [
+    # (name, fmt, has_zeros, has_gidx, dtype): the 32x32x16 kernel (fp16),
+    # the same after the act-order gather (a 4.4 GB workspace), the wide
+    # kernel (bf16)
+    ("awq-fp16-g128-z", "awq", True, False, "fp16"),
+    ("std-fp16-g128-z-act", "std", True, True, "fp16"),
+    ("std-bf16-g128-sym", "std", False, False, "bf16"),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("v", BIG_X_VARIANTS, ids=[v[0] for v in BIG_X_VARIANTS])
+def test_linear_activations_beyond_4gib(W, v):
+    import torch
+    name, fmt, has_z, has_g, dtype = v
+    K, N, gs = 32768, 256, 128
+    edge = (1 << 32) // (2 * K)          # first row starting at byte 2^32 of x
+    M = edge + 1024 + 37                 # 4.36 GB of activations, ragged last tile
+    G = K // gs
+    rng = seeded(315, K, N, int(has_z), int(has_g), len(name))
+    lo, hi = (0.002, 0.02) if dtype == "fp16" else (0.001, 0.01)
+    qweight = random_words(rng, (K, N // 8) if fmt == "awq" else (K // 8, N))
+    qzeros = random_words(rng, (G, N // 8)) if has_z else None
+    scales = uniform_scales(rng, (G, N), lo, hi, dtype)
+    g_idx = actorder_gidx(rng, K, gs) if has_g else None
+    Lyr = _prepare(W, fmt, K, N, gs, has_z, has_g, dtype, qweight, qzeros, scales, g_idx)
+    say(f"{name} M={M} K={K} kernel={Lyr.kernel_name(M)}")
+    # seeded N(0, 1) activations drawn on the device, 8192 rows at a time
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(316)
+    x = torch.empty((M, K), dtype=act_dtype(dtype), device="cuda")
+    for r0 in range(0, M, 8192):
+        r1 = min(M, r0 + 8192)
+        x[r0:r1] = torch.randn((r1 - r0, K), generator=gen, device="cuda")
+    y = filled((M + 2, N), act_dtype(dtype), 0x7F)
+    Lyr.apply(x, out=y[:M])
+    _sync()
+    assert (to_host(y[M:]).view(np.uint16) == 0x7F7F).all(), "write past row M"
+    for r0, r1 in ((0, 64), (edge - 32, edge + 32), (M - 64, M)):
+        xs = to_host(x[r0:r1])
+        ref = O.reference_linear(xs, fmt, dtype, qweight, qzeros, scales, gs, g_idx=g_idx)
+        _assert_close(to_host(y[r0:r1]), ref, dtype, f"{name} rows {r0}..{r1}")
+    del x, y
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
 # Grouped (mixture-of-experts) layer
 # ----------------------------------------------------------------------------
 

@@ -155,3 +155,33 @@ def test_w4a8_full_size_complete(W, v):
         y = lyr.apply_fp8(to_dev(x), xs)
         torch.cuda.synchronize()
         _check(to_host(y), ref, dtype, f"{label} M={M} (all {M * N} outputs)")
+
+
+@pytest.mark.timeout(600)
+def test_w4a8_codes_beyond_4gib(W):
+    # the fp8 codes span more than 4 GiB (M K bytes): rows at both ends and
+    # across the 4 GiB mark, and a ragged last tile, against the oracle
+    import torch
+    K, N, gs = 65536, 256, 128
+    edge = (1 << 32) // K                # first row starting at byte 2^32 of the codes
+    M = edge + 512 + 37
+    lyr, (qw, qz, sc, gi) = _layer(W, "awq", K, N, gs, True, False, "fp16", 11)
+    q, z = O.codes_from_inputs("awq", qw, qz)
+    Wd = O.dequant(q, z, O.act_to_f64(sc, "fp16"), O.group_index(K, gs, gi))
+    del q, z
+    say(f"w4a8 beyond 4 GiB M={M} K={K} kernel={W.w4a8_kernel_name(lyr.layer, M)}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1306)
+    x = torch.empty((M, K), dtype=torch.float16, device="cuda")
+    for r0 in range(0, M, 4096):
+        r1 = min(M, r0 + 4096)
+        x[r0:r1] = torch.randn((r1 - r0, K), generator=gen, device="cuda")
+    xs = torch.tensor([SX], dtype=torch.float32, device="cuda")
+    y = lyr.apply_fp8(x, xs)
+    torch.cuda.synchronize()
+    for r0, r1 in ((0, 32), (edge - 16, edge + 16), (M - 32, M)):
+        xh = to_host(x[r0:r1])
+        xq = O.e4m3_to_f64(O.quantize_acts_fp8(xh, "fp16", SX)) * float(np.float32(SX))
+        _check(to_host(y[r0:r1]), O.linear_ref(xq, Wd), "fp16", f"rows {r0}..{r1}")
+    del x, y
+    torch.cuda.empty_cache()
