@@ -90,13 +90,15 @@ w4_status w4_check_layer(const w4_layer* layer);
 /* Fill *out with the byte sizes of the layer's buffers.  Host only. */
 w4_status w4_sizes(const w4_layer* layer, w4_sizes_t* out);
 
-/* Bytes of scratch device memory w4a16_linear needs for M rows, in three
+/* Bytes of scratch device memory w4a16_linear needs for M rows, in
  * 256-byte-aligned parts: the activations gathered through perm (act-order,
  * M K 2 bytes) or zero-padded to whole 128-row blocks (K tails); split-K
  * fp32 partials [splits][M][N] (16 < M <= 256 on layers with N <= 16384);
- * and, for bf16 from M = 256 (M = 64 on layers with K >= 16384 or
- * N > 16384), fp32 row sums of x per scale period [Kp / L][M] (L = the group
- * size, at most 128).  0 when none applies (fp16 with K % 128 == 0 and no
+ * for bf16 on the wide kernel from M = 256 (M = 64 on layers with
+ * K >= 16384 or N > 16384), fp32 row sums of x per scale period [Kp / L][M]
+ * (L = the group size, at most 128); and for bf16 on the large-M kernel
+ * (at least 256 tiles of 128 x 256 outputs), an fp16 copy of x [M][Kp] and
+ * fp32 row factors [M].  0 when none applies (fp16 with K % 128 == 0 and no
  * act-order outside the split-K range, for instance).  Host only. */
 w4_status w4_workspace_size(const w4_layer* layer, int64_t M, size_t* bytes);
 
@@ -182,8 +184,9 @@ w4_status w4_repack_gptq(const w4_layer* layer, const int32_t* std_qweight, cons
  *                  gathered through perm; with K % 128 != 0, x padded with
  *                  zero columns to Kp; for 16 < M <= 256 on layers with
  *                  N <= 16384 it also holds the fp32 split-K partials
- *                  [splits][M][N].  Calls that overlap in time must not
- *                  share a workspace.
+ *                  [splits][M][N]; for bf16 the row sums or the fp16 copy
+ *                  of x (w4_workspace_size).  Calls that overlap in time
+ *                  must not share a workspace.
  * Accuracy: within max|y - ref| <= 1e-2 (1 + |ref|) elementwise and
  * relative Frobenius error <= 2e-3 of the float64 reference. */
 w4_status w4a16_linear(const w4_layer* layer, int64_t M, const void* x, const int32_t* tiled_qweight,
@@ -200,6 +203,10 @@ w4_status w4a16_linear(const w4_layer* layer, int64_t M, const void* x, const in
  * current, so make the first call outside graph capture.
  *   W4_ERR_WORKSPACE  the call needs more than w4_noalloc_scratch_bytes()
  *                     (w4_workspace_size() tells how much it needs)
+ * A bf16 call whose large-M kernel would need an fp16 copy of x larger than
+ * the array runs the wide kernel instead (within the same accuracy bound;
+ * its row sums need M K / 32 bytes at most), so only that call's kernel can
+ * differ from w4a16_linear's.
  * Every call on a device shares that device's array, which keeps the last
  * call's contents (nothing in it needs to start at zero): calls that overlap
  * in time on one device race, whatever their streams. */

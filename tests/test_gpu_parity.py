@@ -523,11 +523,11 @@ def test_linear_full_size(W, c, M):
 # to 1024 strips, two waves beyond, and an odd strip count);
 # K = 1152 is nine 128-row blocks, so every pipeline depth runs full trips and
 # a partial tail, and a 4-way split gives uneven K ranges (2, 2, 2, 3).
-WIDE_TILE_SHAPES = [(1024, 16384), (256, 32768), (64, 32768), (32, 32768), (40, 8192), (24, 8192), (200, 8192),
+WIDE_TILE_SHAPES = [(1024, 4096), (256, 32768), (64, 32768), (32, 32768), (40, 8192), (24, 8192), (200, 8192),
                     (16, 12288), (9, 20480), (300, 4104), (16, 16392),
-                    # fp16 with >= 256 tiles of 128 x 256: the 32x32x16 kernel, with
-                    # ragged row tiles, a padded half strip and a partial 256-column
-                    # tile
+                    # >= 256 tiles of 128 x 256: the 32x32x16 kernel (bf16 on the
+                    # exact fp16 copy of x), with ragged row tiles, a padded half
+                    # strip and a partial 256-column tile
                     (1100, 8200), (2000, 8192)]
 WIDE_VARIANTS = [
     # (name, fmt, group_size, has_zeros, has_gidx, dtype, K)
@@ -538,9 +538,10 @@ WIDE_VARIANTS = [
     ("std-fp16-ch-z", "std", -1, True, False, "fp16", 1152),
     ("std-fp16-g128-z-act", "std", 128, True, True, "fp16", 1152),
     ("std-fp16-g64-sym", "std", 64, False, False, "fp16", 1152),
-    # bf16 at M >= 256 (and M = 64 on wide layers) reads the row sums of a
-    # pre-pass: four sums per block at g = 32, and act-order (sums of the
-    # gathered columns)
+    # bf16 on the wide kernel at M >= 256 (and M = 64 on wide layers) reads
+    # the row sums of a pre-pass: four sums per block at g = 32, and
+    # act-order (sums of the gathered columns); on the 32x32x16 kernel it
+    # converts the (gathered) activations to fp16 first
     ("std-bf16-g32-z", "std", 32, True, False, "bf16", 1152),
     ("std-bf16-g128-z-act", "std", 128, True, True, "bf16", 1152),
     # K tails: nine blocks after padding, the last one partly padding
@@ -571,6 +572,80 @@ def test_linear_wide_tiles_sampled(W, v):
 
 
 # ----------------------------------------------------------------------------
+# bf16 at large M: the 32x32x16 kernel on an exact fp16 copy of x, each row
+# scaled by a power of two into fp16's exact range
+# ----------------------------------------------------------------------------
+
+def _bf16_rows_scaled(x_bits, k):
+    """bf16 x with row m multiplied by 2^k[m] (exact while the values stay
+    normal; smaller ones round to bf16's subnormal grid)."""
+    v = O.bf16_to_f64(x_bits) * np.exp2(k.astype(np.float64))[:, None]
+    return to_bf16_bits(v.astype(np.float32))
+
+
+def test_linear_bf16_large_m_row_scaling(W):
+    """Each row of x is multiplied by the power of two that brings its
+    largest magnitude into [2^14, 2^15) before the fp16 conversion, and its
+    result by the inverse.  So multiplying a row of x by 2^k multiplies its
+    result by 2^k bit for bit (no bias, results normal), for k from -100 to
+    100; an all-zero row gives zeros; rows near 2^-120, whose exponent the
+    conversion clamps, still match the oracle (compared after scaling both by
+    2^120)."""
+    K, N, gs, M = 1152, 8200, 128, 1100
+    G = K // gs
+    rng = seeded(515, K, N)
+    qweight = random_words(rng, (K // 8, N))
+    qzeros = random_words(rng, (G, N // 8))
+    scales = uniform_scales(rng, (G, N), 0.001, 0.01, "bf16")
+    Lyr = _prepare(W, "std", K, N, gs, True, False, "bf16", qweight, qzeros, scales, None)
+    say(f"bf16 row scaling M={M} kernel={Lyr.kernel_name(M)}")
+    assert Lyr.kernel_name(M).startswith("w4_big"), Lyr.kernel_name(M)
+    x0 = normal_acts(seeded(516, M, K), (M, K), "bf16")
+    ks = np.array([-100, -61, -21, -1, 0, 1, 7, 15, 16, 17, 33, 100])
+    k = ks[np.arange(M) % len(ks)]
+    zero_row, tiny = M - 3, [M - 2, M - 1]
+    k[tiny] = -120
+    x = _bf16_rows_scaled(x0, k)
+    x[zero_row] = 0
+    y0, _ = _run_linear(W, Lyr, x0)
+    y, _ = _run_linear(W, Lyr, x)
+    ref0 = O.reference_linear(x0, "std", "bf16", qweight, qzeros, scales, gs)
+    _assert_strict(y0, ref0, "bf16", "unscaled rows")
+    y0f, yf = O.bf16_to_f64(y0), O.bf16_to_f64(y)
+    expected = y0f * np.exp2(k.astype(np.float64))[:, None]
+    rows = np.ones(M, dtype=bool)
+    rows[[zero_row, *tiny]] = False
+    cmp = rows[:, None] & ((expected == 0) | (np.abs(expected) >= 2.0 ** -120))
+    bad = cmp & (yf != expected)
+    assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[:4])
+    say(f"  2^k scaling exact on {int(cmp.sum())} outputs")
+    assert (yf[zero_row] == 0).all()
+    ref_t = O.reference_linear(x[tiny], "std", "bf16", qweight, qzeros, scales, gs) * 2.0 ** 120
+    y_t = to_bf16_bits((yf[tiny] * 2.0 ** 120).astype(np.float32))
+    _assert_close(y_t, ref_t, "bf16", "rows near 2^-120, times 2^120")
+
+
+def test_linear_bf16_large_m_long_k(W):
+    """bf16 at large M with K > 32768, where the conversion pre-pass reads
+    each row twice instead of keeping it in registers: every column of the
+    first and the last 48 rows against the oracle."""
+    K, N, gs, M = 33792, 4104, 128, 2000
+    G = K // gs
+    rng = seeded(517, K, N)
+    qweight = random_words(rng, (K // 8, N))
+    scales = uniform_scales(rng, (G, N), 0.001, 0.01, "bf16")
+    Lyr = _prepare(W, "std", K, N, gs, False, False, "bf16", qweight, None, scales, None)
+    say(f"bf16 long K M={M} K={K} kernel={Lyr.kernel_name(M)}")
+    assert Lyr.kernel_name(M).startswith("w4_big"), Lyr.kernel_name(M)
+    x = normal_acts(seeded(518, M, K), (M, K), "bf16")
+    y, guard = _run_linear(W, Lyr, x, guard_rows=1)
+    assert (guard.view(np.uint16) == 0x7F7F).all(), "write past row M"
+    rows = np.r_[0:48, M - 48:M]
+    ref = O.reference_linear(x[rows], "std", "bf16", qweight, None, scales, gs)
+    _assert_strict(y[rows], ref, "bf16", "first and last 48 rows")
+
+
+# ----------------------------------------------------------------------------
 # HIP graph capture: replays match the eager launch bit for bit
 # ----------------------------------------------------------------------------
 
@@ -580,11 +655,14 @@ def test_linear_wide_tiles_sampled(W, v):
                                               (40, 1120, 32, False, "fp16"), (300, 1120, 32, False, "fp16"),
                                               (1100, 1120, 32, False, "fp16"),
                                               # bf16 row-sum pre-pass (with act-order and with a K tail)
-                                              (300, 1152, 128, True, "bf16"), (1100, 1120, 32, False, "bf16")])
+                                              (300, 1152, 128, True, "bf16"), (1100, 1120, 32, False, "bf16"),
+                                              # bf16 fp16-copy pre-pass of the 32x32x16 kernel (after
+                                              # the act-order gather)
+                                              (2000, 1152, 128, True, "bf16")])
 def test_linear_hip_graph_replays_match_eager(W, M, K, gs, act, dtype):
     # act-order (gather into the workspace), K tails (zero-padded copy into
-    # the workspace) and the bf16 row sums (a pre-pass into the workspace)
-    # inside a captured graph
+    # the workspace) and the bf16 row sums or fp16 copy (pre-passes into the
+    # workspace) inside a captured graph
     import torch
     N = 4096
     G = K // gs
@@ -699,12 +777,14 @@ def test_linear_smallest_layers(W, dtype):
 # ----------------------------------------------------------------------------
 
 BIG_X_VARIANTS = [
-    # (name, fmt, has_zeros, has_gidx, dtype): the 32x32x16 kernel (fp16),
-    # the same after the act-order gather (a 4.4 GB workspace), the wide
-    # kernel (bf16)
-    ("awq-fp16-g128-z", "awq", True, False, "fp16"),
-    ("std-fp16-g128-z-act", "std", True, True, "fp16"),
-    ("std-bf16-g128-sym", "std", False, False, "bf16"),
+    # (name, fmt, has_zeros, has_gidx, dtype, K, M or 0): the 32x32x16 kernel
+    # (fp16), the same after the act-order gather (a 4.4 GB workspace), and
+    # for bf16 on its fp16 copy of x (conversion pre-pass, 4.4 GB); the wide
+    # kernel (bf16 with row sums; fewer than 256 tiles of 128 x 256)
+    ("awq-fp16-g128-z", "awq", True, False, "fp16", 32768, 0),
+    ("std-fp16-g128-z-act", "std", True, True, "fp16", 32768, 0),
+    ("std-bf16-g128-sym", "std", False, False, "bf16", 32768, 0),
+    ("std-bf16-g128-sym-wide", "std", False, False, "bf16", 66048, 32600),
 ]
 
 
@@ -712,10 +792,10 @@ BIG_X_VARIANTS = [
 @pytest.mark.parametrize("v", BIG_X_VARIANTS, ids=[v[0] for v in BIG_X_VARIANTS])
 def test_linear_activations_beyond_4gib(W, v):
     import torch
-    name, fmt, has_z, has_g, dtype = v
-    K, N, gs = 32768, 256, 128
-    edge = (1 << 32) // (2 * K)          # first row starting at byte 2^32 of x
-    M = edge + 1024 + 37                 # 4.36 GB of activations, ragged last tile
+    name, fmt, has_z, has_g, dtype, K, M = v
+    N, gs = 256, 128
+    edge = (1 << 32) // (2 * K)          # last row starting before byte 2^32 of x
+    M = M or edge + 1024 + 37            # > 4.3 GB of activations, ragged last tile
     G = K // gs
     rng = seeded(315, K, N, int(has_z), int(has_g), len(name))
     lo, hi = (0.002, 0.02) if dtype == "fp16" else (0.001, 0.01)

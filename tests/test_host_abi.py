@@ -230,7 +230,15 @@ def test_split_k_workspace_is_sized_and_checked(W):
     # per 128-row block follow, [K / 128][M] fp32; above 128 rows a K of
     # 8192 splits two ways
     assert W.w4_workspace_size(L, 256) == 2 * 256 * 8192 * 4 + 64 * 256 * 4
-    assert W.w4_workspace_size(L, 2048) == 64 * 2048 * 4
+    # with >= 256 tiles of 128 x 256 the 32x32x16 kernel runs on an fp16
+    # copy of x [M][K] and its row factors [M] fp32
+    assert W.w4_kernel_name(L, 2048) == "w4_big_128x256"
+    assert W.w4_workspace_size(L, 2048) == 2048 * 8192 * 2 + 2048 * 4
+    assert W.w4_workspace_size(L, 1000) == 1000 * 8192 * 2 + (1000 * 4 + 255) // 256 * 256
+    # fewer tiles: the 128 x 128 wide tile with row sums
+    L4 = W.make_layer(8192, 4096, 128, False, False, "bf16")
+    assert W.w4_kernel_name(L4, 1024) == "w4_wide_128x128"
+    assert W.w4_workspace_size(L4, 1024) == 64 * 1024 * 4
     # a longer K splits eight ways (four at M = 256)
     L2 = W.make_layer(28672, 8192, 128, False, False, "bf16")
     assert W.w4_workspace_size(L2, 32) == 8 * 32 * 8192 * 4

@@ -44,6 +44,16 @@
 // in the wide kernel), passes one barrier, issues block b + S - 1 and
 // computes block b.
 //
+// bf16 layers run the same fp16 kernel: a pre-pass (bf16_rows_to_f16)
+// converts x to fp16.  A bf16 value has 8 significant bits and an fp16
+// normal 11, so every bf16 value in fp16's normal range converts without
+// rounding.  Each row is first multiplied by the power of two 2^-e (exact)
+// that brings its largest finite magnitude into [2^14, 2^15), and the
+// epilogue multiplies that row's result by 2^e.  So every value of the row
+// down to 2^-29 of its largest is exact; smaller ones are rounded to fp16's
+// subnormal grid, an error below 2^-40 of the row's largest magnitude per
+// element.  Scales, bias and output stay bf16.
+//
 // Workgroup -> tile: the dispatcher hands consecutive workgroups to the
 // eight XCDs in turn; the grid is remapped so that each XCD walks a
 // contiguous range of tiles, in bands of group_m row tiles, so tiles that
@@ -89,8 +99,14 @@ __device__ __forceinline__ void big_tile_of(int64_t L, int64_t tiles_m, int64_t 
 // experts); expert e owns rows [offs[e], offs[e + 1]) of x and y (clamped
 // into the M rows given) and the e-th copy of the tiled weights, scales,
 // zeros and bias, each following the previous expert's.
-template <int WM, int WN, int MT, int NT, int S, int GM, bool HAS_Z, bool GROUPED = false>
-__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __restrict__ x_in,
+//
+// OB16: a bf16 layer (bf16 scales, bias and output) on fp16 activations from
+// bf16_rows_to_f16, with rowf[m] = 2^e the factor of row m.  Plain launches.
+// With one scale period per block it is held to two waves per SIMD, as the
+// fp16 kernel runs: left free, the compiler takes two registers more than
+// that allows (with zero points) and one wave per SIMD runs.
+template <int WM, int WN, int MT, int NT, int S, int GM, bool HAS_Z, bool GROUPED = false, bool OB16 = false>
+__global__ __launch_bounds__(64 * WM * WN, OB16 && Groups<GM>::kPeriods == 1 ? 2 : 1) void gemm_big(const uint16_t* __restrict__ x_in,
                                                              const u4* __restrict__ qw_in,
                                                              const uint16_t* __restrict__ sc_in,
                                                              const uint32_t* __restrict__ zs_in,
@@ -98,8 +114,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
                                                              uint16_t* __restrict__ y_in, int64_t M_in, int64_t K,
                                                              int64_t N, int G,
                                                              int64_t tiles_m, int64_t tiles_n, int64_t group_m,
-                                                             const int32_t* __restrict__ offs) {
+                                                             const int32_t* __restrict__ offs,
+                                                             const float* __restrict__ rowf) {
   using C = BigCfg<WM, WN, MT, NT, S>;
+  static_assert(!(OB16 && GROUPED), "bf16 layers: plain launches");
   constexpr int NP = Groups<GM>::kPeriods;  // scale periods per 128-row block
   constexpr int SPP = 8 / NP;               // 16-deep steps per period
   constexpr int NA = C::NA;
@@ -237,7 +255,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
         const uint32_t z = HAS_Z ? (r.z[nt][p] >> zshift) & 0xFu : 8u;
         n1[nt] = nz1024_bits(z);
         n2[nt] = nz64_bits(z);
-        const float s_cur = act_to_f32<false>(r.s[nt][p]);
+        const float s_cur = act_to_f32<OB16>(r.s[nt][p]);
         ratio[nt] = s_prev[nt] * __builtin_amdgcn_rcpf(s_cur);
         s_prev[nt] = s_cur;
       }
@@ -294,19 +312,49 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
 
   // epilogue: element r of lane l is row 8 (r / 4) + 4 h + r % 4 of each row
   // tile, column c of each column tile
+  if constexpr (OB16) {
+    // row tile by row tile, so that only one tile's row factors are live:
+    // rowf[m .. m + 3] for m = 8 j + 4 h of the tile (rowf holds whole
+    // 128-row tiles; rows >= M are never stored)
+    float bv[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int64_t n = n0 + (int64_t)(wn * NT + nt) * 32 + c;
-    if (n >= N) continue;  // padded columns, or tiles past the last strip
-    const float bv = bias != nullptr ? act_to_f32<false>(bias[n]) : 0.f;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int64_t n = n0 + (int64_t)(wn * NT + nt) * 32 + c;
+      bv[nt] = bias != nullptr && n < N ? act_to_f32<true>(bias[n]) : 0.f;
+    }
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i) {
+      const int64_t mb = m0 + (int64_t)(wm * MT + i) * 32 + 4 * h;
+      f4 rf[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + (int64_t)(wm * MT + i) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m >= M) continue;
-        y[m * N + n] = f32_to_act<false>(acc[i][nt][r] * s_prev[nt] + bv);
+      for (int j = 0; j < 4; ++j) rf[j] = *reinterpret_cast<const f4*>(rowf + mb + 8 * j);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int64_t n = n0 + (int64_t)(wn * NT + nt) * 32 + c;
+        if (n >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = mb + 8 * (r >> 2) + (r & 3);
+          if (m >= M) continue;
+          y[m * N + n] = f32_to_act<true>(acc[i][nt][r] * s_prev[nt] * rf[r >> 2][r & 3] + bv[nt]);
+        }
       }
+    }
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int64_t n = n0 + (int64_t)(wn * NT + nt) * 32 + c;
+      if (n >= N) continue;  // padded columns, or tiles past the last strip
+      const float bv = bias != nullptr ? act_to_f32<false>(bias[n]) : 0.f;
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = m0 + (int64_t)(wm * MT + i) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (m >= M) continue;
+          y[m * N + n] = f32_to_act<false>(acc[i][nt][r] * s_prev[nt] + bv);
+        }
+    }
   }
   };
 
@@ -342,16 +390,103 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big(const uint16_t* __re
   }
 }
 
-// Launch of one configuration (fp16 only, the whole of K per workgroup);
-// `group_m` row tiles per band of the tile order.
-template <int WM, int WN, int MT, int NT, int S, int GM, bool HZ>
-hipError_t run_big(const Args& a, const uint16_t* x, int64_t group_m, hipStream_t st) {
+// xh[m][k] = fp16(x[m][k] 2^-e_m) and rowf[m] = 2^e_m for bf16 x [M][K]
+// (K a multiple of 8): e_m brings the row's largest finite magnitude into
+// [2^14, 2^15) (clamped to [-126, 113]; 0 for a row without a finite nonzero
+// value).  One workgroup
+// per row: the row's maximum first, then the conversion (round to nearest
+// even, exact in fp16's normal range).  CH > 0: rows of at most 256 CH
+// 16-byte chunks, kept in registers between the two passes (one read of x);
+// CH = 0: any K, read twice.
+template <int CH>
+__global__ __launch_bounds__(256) void bf16_rows_to_f16(const uint16_t* __restrict__ x, uint16_t* __restrict__ xh,
+                                                        float* __restrict__ rowf, int64_t M, int64_t K) {
+  __shared__ float red[4];
+  const int64_t K8 = K / 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto upd = [](float& mx, const u4& v) __attribute__((always_inline)) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = __builtin_fabsf(bit_as<float>(w[j] << 16));
+      const float hi = __builtin_fabsf(bit_as<float>(w[j] & 0xFFFF0000u));
+      // infinities and NaNs leave the row unscaled (they stay what they are)
+      if (lo < __builtin_inff() && lo > mx) mx = lo;
+      if (hi < __builtin_inff() && hi > mx) mx = hi;
+    }
+  };
+  auto cvt = [](const u4& v, float down) __attribute__((always_inline)) -> u4 {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = (uint32_t)f32_to_act<false>(bit_as<float>(w[j] << 16) * down) |
+             ((uint32_t)f32_to_act<false>(bit_as<float>(w[j] & 0xFFFF0000u) * down) << 16);
+    return u4{o[0], o[1], o[2], o[3]};
+  };
+  for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+    const u4* src = reinterpret_cast<const u4*>(x + m * K);
+    u4* dst = reinterpret_cast<u4*>(xh + m * K);
+    float mx = 0.f;
+    u4 keep[CH > 0 ? CH : 1];
+    if constexpr (CH > 0) {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int64_t c = threadIdx.x + 256 * j;
+        keep[j] = c < K8 ? src[c] : u4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < CH; ++j) upd(mx, keep[j]);
+    } else {
+      for (int64_t c = threadIdx.x; c < K8; c += 256) upd(mx, src[c]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, off));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    __syncthreads();  // red is rewritten for the next row
+    // exponent of mx (-127 for a subnormal mx, which the clamp covers: every
+    // bf16 value is at least 2^-133 and so stays exact after 2^126)
+    const int ex = (int)((bit_as<uint32_t>(mx) >> 23) & 0xFFu) - 127;
+    const int e = mx > 0.f ? (ex - 14 < -126 ? -126 : ex - 14) : 0;
+    const float down = bit_as<float>((uint32_t)(127 - e) << 23);
+    if (threadIdx.x == 0) rowf[m] = bit_as<float>((uint32_t)(127 + e) << 23);
+    if constexpr (CH > 0) {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int64_t c = threadIdx.x + 256 * j;
+        if (c < K8) dst[c] = cvt(keep[j], down);
+      }
+    } else {
+      for (int64_t c = threadIdx.x; c < K8; c += 256) dst[c] = cvt(src[c], down);
+    }
+  }
+}
+
+// Launch of one configuration (the whole of K per workgroup); `group_m` row
+// tiles per band of the tile order.  OB16: x is bf16, converted into xh
+// ([M][K] fp16) and rowf ([M] fp32) first.
+template <int WM, int WN, int MT, int NT, int S, int GM, bool HZ, bool OB16 = false>
+hipError_t run_big(const Args& a, const uint16_t* x, uint16_t* xh, float* rowf, int64_t group_m, hipStream_t st) {
   using C = BigCfg<WM, WN, MT, NT, S>;
   const int64_t Np = (a.N + kTileN - 1) / kTileN * kTileN;
   const int64_t tiles_m = (a.M + C::BM - 1) / C::BM, tiles_n = (Np + C::BN - 1) / C::BN;
   if (tiles_m * tiles_n > 0x7FFFFFFF || group_m < 1) return hipErrorInvalidValue;
-  gemm_big<WM, WN, MT, NT, S, GM, HZ><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
-      x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N, a.G, tiles_m, tiles_n, group_m, nullptr);
+  if constexpr (OB16) {
+    if (xh == nullptr || rowf == nullptr || a.K % 8 != 0) return hipErrorInvalidValue;
+    const unsigned blocks = (unsigned)(a.M < 65535 ? a.M : 65535);
+    if (a.K <= 8 * 256 * 16)
+      bf16_rows_to_f16<16><<<blocks, 256, 0, st>>>(x, xh, rowf, a.M, a.K);
+    else
+      bf16_rows_to_f16<0><<<blocks, 256, 0, st>>>(x, xh, rowf, a.M, a.K);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    x = xh;
+  }
+  gemm_big<WM, WN, MT, NT, S, GM, HZ, false, OB16><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
+      x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N, a.G, tiles_m, tiles_n, group_m, nullptr,
+      OB16 ? rowf : nullptr);
   return hipGetLastError();
 }
 
@@ -368,8 +503,52 @@ hipError_t run_big_grouped(const Args& a, hipStream_t st) {
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)tiles_n, (unsigned)tiles_m, (unsigned)a.groups);
   gemm_big<WM, WN, MT, NT, S, GM, HZ, true><<<grid, 64 * WM * WN, 0, st>>>(
-      a.x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N, a.G, tiles_m, tiles_n, 1, a.offs);
+      a.x, a.qw, a.sc, a.zs, a.bias, a.y, a.M, a.K, a.N, a.G, tiles_m, tiles_n, 1, a.offs, nullptr);
   return hipGetLastError();
+}
+
+// The shipped configuration: four waves side by side, each 128 rows x 64
+// columns (workgroup tile 128 x 256), double-buffered (64 KiB of LDS, two
+// workgroups per CU); tile order in bands of four row tiles.  Chosen from
+// sweeps of the prefill shapes on MI355X against 2 x 2 and 2 x 4 wave
+// arrangements, 64 x 64 and 64 x 128 wave tiles and three- and four-deep
+// pipelines.
+constexpr int kBigWM = 1, kBigWN = 4, kBigMT = 4, kBigNT = 2, kBigS = 2;
+constexpr int64_t kBigGroupM = 4;
+
+template <int GM, bool OB16>
+hipError_t big_z(const Args& a, const uint16_t* x, uint16_t* xh, float* rowf, bool has_z, hipStream_t st) {
+  return has_z ? run_big<kBigWM, kBigWN, kBigMT, kBigNT, kBigS, GM, true, OB16>(a, x, xh, rowf, kBigGroupM, st)
+               : run_big<kBigWM, kBigWN, kBigMT, kBigNT, kBigS, GM, false, OB16>(a, x, xh, rowf, kBigGroupM, st);
+}
+
+template <bool OB16>
+hipError_t big_gm(const Args& a, const uint16_t* x, uint16_t* xh, float* rowf, bool has_z, hipStream_t st) {
+  switch (group_mode(a.gs, a.K)) {
+    case GM_32: return big_z<GM_32, OB16>(a, x, xh, rowf, has_z, st);
+    case GM_64: return big_z<GM_64, OB16>(a, x, xh, rowf, has_z, st);
+    case GM_128: return big_z<GM_128, OB16>(a, x, xh, rowf, has_z, st);
+    default: return big_z<GM_CH, OB16>(a, x, xh, rowf, has_z, st);
+  }
+}
+
+// Arguments of a plain large-M launch.
+inline Args big_args(const Shape& s, int64_t M, const int32_t* tiled_w, const void* tiled_s, const int32_t* tiled_z,
+                     const void* bias, void* y) {
+  Args a{};
+  a.qw = reinterpret_cast<const u4*>(tiled_w);
+  a.sc = static_cast<const uint16_t*>(tiled_s);
+  a.zs = reinterpret_cast<const uint32_t*>(tiled_z);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.y = static_cast<uint16_t*>(y);
+  a.part = nullptr;
+  a.splits = 1;
+  a.M = M;
+  a.K = s.K;
+  a.N = s.N;
+  a.G = s.G;
+  a.gs = s.gs;
+  return a;
 }
 
 }  // namespace

@@ -18,7 +18,8 @@ inline size_t front_bytes(const Shape& s, const GemmPlan& p, int64_t M) {
 
 // Workspace layout: front bytes (gathered or padded activations), split-K
 // partials [splits][M][N] fp32, row sums [Kp / L][M] fp32 (bf16 pre-pass),
-// each part 256-byte aligned.
+// the fp16 copy of x and its row factors (bf16 on the large-M kernel), each
+// part 256-byte aligned.
 size_t partial_bytes(const Shape& s, const GemmPlan& p, int64_t M) {
   const size_t b = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)s.N * sizeof(float) : 0;
   return (b + 255) / 256 * 256;
@@ -28,6 +29,15 @@ size_t rowsum_bytes(const Shape& sp, const GemmPlan& p, int64_t M) {
   if (!p.rsin) return 0;
   const size_t periods = (size_t)(sp.Kp / kTileK) * (size_t)(sp.gs == 32 ? 4 : (sp.gs == 64 ? 2 : 1));
   return (periods * (size_t)M * sizeof(float) + 255) / 256 * 256;
+}
+
+// bf16 on the large-M kernel: the fp16 copy of x [M][Kp], then the row
+// factors [M] fp32
+size_t h16_x_bytes(const Shape& sp, const GemmPlan& p, int64_t M) {
+  return p.h16 ? ((size_t)M * (size_t)sp.Kp * sizeof(uint16_t) + 255) / 256 * 256 : 0;
+}
+size_t h16_bytes(const Shape& sp, const GemmPlan& p, int64_t M) {
+  return p.h16 ? h16_x_bytes(sp, p, M) + ((size_t)M * sizeof(float) + 255) / 256 * 256 : 0;
 }
 
 // Act-order first gathers the columns of x into the workspace (front bytes
@@ -71,11 +81,11 @@ hipError_t pick_flags(const Shape& s, const Args& a, hipStream_t st) {
 }  // namespace
 
 namespace {
-GemmPlan plan_tiles(const Shape& s, int64_t M);
+GemmPlan plan_tiles(const Shape& s, int64_t M, bool bf16_big);
 }  // namespace
 
-GemmPlan plan_gemm(const Shape& s, int64_t M) {
-  GemmPlan p = plan_tiles(s, M);
+GemmPlan plan_gemm(const Shape& s, int64_t M, bool bf16_big) {
+  GemmPlan p = plan_tiles(s, M, bf16_big);
   // bf16 wide kernels take the zero-point row sums from a pre-pass
   // (row_sums_bf16) instead of a ones-operand MFMA per row tile and step
   // where that measured faster: M >= 256, or M >= 64 on long (K >= 16384)
@@ -84,11 +94,12 @@ GemmPlan plan_gemm(const Shape& s, int64_t M) {
   const int64_t T = s.Np / kTileN;
   if (s.bf16 && p.kind == GemmKind::kWide && (M >= 256 || (M >= 64 && (s.K >= 16384 || T > 1024))))
     p.rsin = true;
+  p.h16 = s.bf16 && p.kind == GemmKind::kBig;
   return p;
 }
 
 namespace {
-GemmPlan plan_tiles(const Shape& s, int64_t M) {
+GemmPlan plan_tiles(const Shape& s, int64_t M, bool bf16_big) {
   // (mt, nb, kw, xl): 16-row tiles per wave, strips per workgroup, waves per
   // workgroup (splitting K), activations staged in LDS; the ring depth
   // follows from them (skinny_depth).  Chosen from timing sweeps of the
@@ -149,7 +160,7 @@ GemmPlan plan_tiles(const Shape& s, int64_t M) {
     } else {
       p = GemmPlan{GemmKind::kSkinny, 1, 1, 8, false, "w4_skinny_k8"};
     }
-  } else if (!s.bf16 && ((M + big_tile_rows() - 1) / big_tile_rows()) *
+  } else if ((!s.bf16 || bf16_big) && ((M + big_tile_rows() - 1) / big_tile_rows()) *
                                 ((s.Np + big_tile_cols() - 1) / big_tile_cols()) >= 256) {
     // large M, fp16, at least one 128 x 256 tile of 32x32x16 MFMAs per CU
     // (with fewer tiles, splitting K measured slower than the wide kernel's
@@ -223,15 +234,27 @@ void gemm_launch_dims(const Shape& s0, int64_t M, unsigned grid[3], unsigned* th
   }
 }
 
-size_t gemm_workspace_bytes(const Shape& s, int64_t M) {
+namespace {
+size_t plan_bytes(const Shape& s, const Shape& sp, const GemmPlan& p, int64_t M) {
+  return front_bytes(s, p, M) + partial_bytes(s, p, M) + rowsum_bytes(sp, p, M) + h16_bytes(sp, p, M);
+}
+
+// The plan of a call with at most ws_cap bytes of workspace (s unpadded).
+GemmPlan plan_capped(const Shape& s, int64_t M, size_t ws_cap) {
   const Shape sp = padded_k(s);
   const GemmPlan p = plan_gemm(sp, M);
-  return front_bytes(s, p, M) + partial_bytes(s, p, M) + rowsum_bytes(sp, p, M);
+  if (p.h16 && plan_bytes(s, sp, p, M) > ws_cap) return plan_gemm(sp, M, false);
+  return p;
+}
+}  // namespace
+
+size_t gemm_workspace_bytes(const Shape& s, int64_t M, size_t ws_cap) {
+  return plan_bytes(s, padded_k(s), plan_capped(s, M, ws_cap), M);
 }
 
 hipError_t launch_gemm(const Shape& s0, int64_t M, const void* x, const int32_t* tiled_w, const void* tiled_s,
                        const int32_t* tiled_z, const int32_t* perm, const void* bias, void* y, void* ws,
-                       hipStream_t st) {
+                       hipStream_t st, size_t ws_cap) {
   // the kernels run the padded shape (K a whole number of blocks)
   const Shape s = padded_k(s0);
   Args a;
@@ -253,7 +276,7 @@ hipError_t launch_gemm(const Shape& s0, int64_t M, const void* x, const int32_t*
   a.N = s.N;
   a.G = s.G;
   a.gs = s.gs;
-  const GemmPlan p = plan_gemm(s, M);
+  const GemmPlan p = plan_capped(s0, M, ws_cap);
   const size_t front = front_bytes(s0, p, M);
   if (s0.K != s0.Kp) {
     // zero-padded copy of x in the workspace (act-order is excluded here)
@@ -276,7 +299,14 @@ hipError_t launch_gemm(const Shape& s0, int64_t M, const void* x, const int32_t*
       if (e != hipSuccess) return e;
       xb = xp;
     }
-    return launch_big(s, M, xb, tiled_w, tiled_s, tiled_z, bias, y, st);
+    uint16_t* xh = nullptr;
+    float* rowf = nullptr;
+    if (p.h16) {
+      char* h = static_cast<char*>(ws) + front + partial_bytes(s, p, M) + rowsum_bytes(s, p, M);
+      xh = reinterpret_cast<uint16_t*>(h);
+      rowf = reinterpret_cast<float*>(h + h16_x_bytes(s, p, M));
+    }
+    return launch_big(s, M, xb, tiled_w, tiled_s, tiled_z, bias, y, xh, rowf, st);
   }
   Shape sk = s;
   if (s.has_perm) {

@@ -81,23 +81,36 @@ struct GemmPlan {
   int wide = 0;    // wide tile configuration (index into the kernel's table)
   int splits = 1;  // wide kernel: K ranges reduced by a second kernel (1 = none)
   bool rsin = false;  // bf16 wide kernel: row sums from a pre-pass instead of ones-operand MFMAs
+  bool h16 = false;   // bf16 layer on the large-M kernel: exact fp16 copy of x from a pre-pass
   int ar = 0;         // skinny kernel: rows of each block's activation tile copied into LDS
                       // by direct-to-LDS loads (4 or 16; 0 = none)
 };
 
-GemmPlan plan_gemm(const Shape& s, int64_t M);
-size_t gemm_workspace_bytes(const Shape& s, int64_t M);
+// bf16_big: let bf16 layers take the large-M kernel (which needs an fp16
+// copy of x in the workspace)
+GemmPlan plan_gemm(const Shape& s, int64_t M, bool bf16_big = true);
+// ws_cap: the most workspace the call can have.  A bf16 plan whose fp16 copy
+// of x would not fit falls back to the wide kernel (whose row sums need
+// M K / 32 bytes at most); the other plans are the same at any cap.
+size_t gemm_workspace_bytes(const Shape& s, int64_t M, size_t ws_cap = SIZE_MAX);
 void gemm_launch_dims(const Shape& s, int64_t M, unsigned grid[3], unsigned* threads);
 hipError_t launch_gemm(const Shape& s, int64_t M, const void* x, const int32_t* tiled_w, const void* tiled_s,
                        const int32_t* tiled_z, const int32_t* perm, const void* bias, void* y, void* ws,
-                       hipStream_t st);
+                       hipStream_t st, size_t ws_cap = SIZE_MAX);
 
-// ---- large-M GEMM on 32x32x16 MFMA tiles, fp16 (w4_big.hip) ----
+// ---- large-M GEMM on 32x32x16 MFMA tiles (w4_big.hip) ----
 int64_t big_tile_rows();
 int64_t big_tile_cols();
 int big_threads();
+// bf16 layers need xh ([M][K] fp16) and rowf ([M] fp32) in the workspace for
+// the exact fp16 copy of x the kernel runs on; fp16 layers ignore them
 hipError_t launch_big(const Shape& s, int64_t M, const uint16_t* x, const int32_t* tiled_w, const void* tiled_s,
-                      const int32_t* tiled_z, const void* bias, void* y, hipStream_t st);
+                      const int32_t* tiled_z, const void* bias, void* y, uint16_t* xh, float* rowf,
+                      hipStream_t st);
+// the bf16 part of launch_big (w4_big_h16.hip)
+hipError_t launch_big_h16(const Shape& s, int64_t M, const uint16_t* x, const int32_t* tiled_w, const void* tiled_s,
+                          const int32_t* tiled_z, const void* bias, void* y, uint16_t* xh, float* rowf,
+                          hipStream_t st);
 // grouped (mixture-of-experts) launch of the same kernel, fp16 only
 hipError_t launch_big_moe(const Shape& s, int experts, int64_t total_rows, int64_t max_rows, const void* x,
                           const int32_t* offsets, const int32_t* tiled_w, const void* tiled_s,

@@ -1,8 +1,10 @@
 // w4a16_linear_noalloc: w4a16_linear for callers that cannot allocate device
 // memory (code under HIP graph capture, serving loops, harnesses that forbid
 // allocation).  The workspace of w4a16_linear (act-order gather, K-tail
-// padding, split-K partials) lives in a file-scope device array instead of a
-// caller buffer.  The kernels are those of w4a16_linear.
+// padding, split-K partials, bf16 row sums or fp16 copy of x) lives in a
+// file-scope device array instead of a caller buffer.  The kernels are those
+// of w4a16_linear, except that a bf16 call at large M whose fp16 copy of x
+// would not fit the array runs the wide kernel instead of the large-M one.
 #include <mutex>
 
 #include "w4_internal.h"
@@ -48,14 +50,14 @@ w4_status w4a16_linear_noalloc(const w4_layer* L, int64_t M, const void* x, cons
   w4_status st = w4::linear_checks(L, M, x, tiled_qweight, tiled_scales, tiled_qzeros, perm, bias, y);
   if (st != W4_OK || M == 0) return st;
   const w4::Shape s = w4::shape_of(L);
-  if (w4::gemm_workspace_bytes(s, M) > kScratchBytes) return W4_ERR_WORKSPACE;
+  if (w4::gemm_workspace_bytes(s, M, kScratchBytes) > kScratchBytes) return W4_ERR_WORKSPACE;
   st = w4::device_status();
   if (st != W4_OK) return st;
   void* ws = nullptr;
   st = scratch_ptr(&ws);
   if (st != W4_OK) return st;
   if (w4::launch_gemm(s, M, x, tiled_qweight, tiled_scales, tiled_qzeros, perm, bias, y, ws,
-                      static_cast<hipStream_t>(stream)) != hipSuccess)
+                      static_cast<hipStream_t>(stream), kScratchBytes) != hipSuccess)
     return W4_ERR_HIP;
   return W4_OK;
 }
