@@ -1,7 +1,8 @@
 """Benchmark of the W4A16 linear layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config all|decode|tiny|mid|prefill|actorder|w4a8|moe] [--compare] [--group-size G]
+                    [--config all|decode|tiny|mid|prefill|actorder|prefill_bf16|w4a8|moe] [--compare]
+                    [--group-size G]
 
 A step is one forward pass of the hot path over every (shape, M) case of the
 decode workload (7B-class layers, M = 1, 4, 16): for each case one
@@ -14,7 +15,8 @@ of a Python call does not starve the GPU between short decode kernels;
 that step.
 
 With ``--config all`` (the default) the line also carries one block per
-workload (decode, tiny, mid-batch, prefill, act-order), so the metric is
+workload (decode, tiny, mid-batch, prefill, act-order, and the prefill shapes
+as bf16 GPTQ layers), so the metric is
 covered over M = 1..8192: each case is timed alone as the median of five
 replays of a graph of back-to-back launches, and each block reports its
 roofline (HBM-bound cases against 8 TB/s on algorithmic bytes, MFMA-bound
@@ -52,13 +54,13 @@ MFMA_F8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 ROTATE_BYTES = 512 << 20       # working set per shape, > 256 MB MALL
 COPY_PROBE_BYTES = 256 << 20   # plain device copy used to calibrate byte counters
 REPLAYS = 5                    # per-case timing: median of this many graph replays
-WORKLOADS = ("decode", "tiny", "mid", "prefill", "actorder", "w4a8")
+WORKLOADS = ("decode", "tiny", "mid", "prefill", "actorder", "prefill_bf16", "w4a8")
 FLOOR_WORKLOADS = ("decode", "tiny")  # the HBM-bound ones that --floor covers
 FLOOR_SWEEP_WGS = (256, 512, 1024, 2048, 4096)
 FLOOR_TAGS = 15      # empty_kernel<0..14> / stream_read<0..14> name the floor cases
 MARKER_TAG = 15      # empty_kernel<15> on one wave: the --markers case separator
 FLOOR_SWEEP_THREADS = (256, 512, 1024)
-CFG_ID = {"tiny": 1, "decode": 2, "mid": 3, "prefill": 4, "actorder": 5}
+CFG_ID = {"tiny": 1, "decode": 2, "mid": 3, "prefill": 4, "actorder": 5, "prefill_bf16": 6}
 # W4A8-fp8 workload: the decode and prefill layers with FP8-E4M3 activations
 # (static per-tensor scale), quantization included in every call
 W4A8_CFGS = (2, 4)

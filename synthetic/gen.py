@@ -1,4 +1,4 @@
-"""Seeded generators for the five W4A16 workloads (see the package docstring).
+"""Seeded generators for the six W4A16 workloads (see the package docstring).
 
 Workloads (shapes, dtypes and value ranges of the layer being exercised):
 
@@ -12,6 +12,8 @@ Workloads (shapes, dtypes and value ranges of the layer being exercised):
              (K,N) in {(8192,28672), (28672,8192), (8192,8192)}
 5. actorder  standard + g_idx, fp16, g=128, zero points; M in {1,16,64,512};
              (K,N) = (8192,8192); plus a per-channel variant (g=-1, no g_idx)
+6. prefill_bf16  the prefill shapes and row counts as standard (GPTQ)
+             symmetric bf16 layers, g=128 (the bf16 large-M path)
 
 fp16 scales are U[0.002, 0.02]; bf16 scales are U[0.001, 0.01]; activations
 are N(0, 1).  Seeds: weights from SeedSequence([cfg_id, K, N, variant]) so one
@@ -88,7 +90,7 @@ def actorder_gidx(rng: np.random.Generator, K: int, group_size: int) -> np.ndarr
 
 @dataclass(frozen=True)
 class ConfigCase:
-    cfg_id: int           # 1..5 in the order of the workload list above
+    cfg_id: int           # 1..6 in the order of the workload list above
     name: str
     fmt: str              # "awq" (input is AWQ-packed) or "std" (standard / GPTQ-packed)
     dtype: str            # "fp16" | "bf16"  (activations, scales, bias, output)
@@ -124,6 +126,8 @@ def _cases():
     out.append(ConfigCase(5, "actorder", "std", "fp16", 128, True, True, 8192, 8192, (1, 16, 64, 512), 0.002, 0.02))
     out.append(ConfigCase(5, "perchannel", "std", "fp16", -1, True, False, 8192, 8192, (1, 16, 64, 512), 0.002, 0.02,
                           variant=1))
+    for K, N in ((8192, 28672), (28672, 8192), (8192, 8192)):
+        out.append(ConfigCase(6, "prefill_bf16", "std", "bf16", 128, False, False, K, N, (2048, 8192), 0.001, 0.01))
     return tuple(out)
 
 
