@@ -231,10 +231,11 @@ def test_split_k_workspace_is_sized_and_checked(W):
     # 8192 splits two ways
     assert W.w4_workspace_size(L, 256) == 2 * 256 * 8192 * 4 + 64 * 256 * 4
     # with >= 256 tiles of 128 x 256 the 32x32x16 kernel runs on an fp16
-    # copy of x [M][K] and its row factors [M] fp32
+    # copy of x [M][K] and its row factors, fp32 for whole 128-row tiles
     assert W.w4_kernel_name(L, 2048) == "w4_big_128x256"
     assert W.w4_workspace_size(L, 2048) == 2048 * 8192 * 2 + 2048 * 4
-    assert W.w4_workspace_size(L, 1000) == 1000 * 8192 * 2 + (1000 * 4 + 255) // 256 * 256
+    assert W.w4_workspace_size(L, 1000) == 1000 * 8192 * 2 + 1024 * 4
+    assert W.w4_workspace_size(L, 1030) == 1030 * 8192 * 2 + 1152 * 4
     # fewer tiles: the 128 x 128 wide tile with row sums
     L4 = W.make_layer(8192, 4096, 128, False, False, "bf16")
     assert W.w4_kernel_name(L4, 1024) == "w4_wide_128x128"

@@ -32,12 +32,13 @@ size_t rowsum_bytes(const Shape& sp, const GemmPlan& p, int64_t M) {
 }
 
 // bf16 on the large-M kernel: the fp16 copy of x [M][Kp], then the row
-// factors [M] fp32
+// factors, fp32 for whole 128-row tiles (the epilogue reads a tile's
+// factors in 16-byte pieces; rows >= M are read, never used)
 size_t h16_x_bytes(const Shape& sp, const GemmPlan& p, int64_t M) {
   return p.h16 ? ((size_t)M * (size_t)sp.Kp * sizeof(uint16_t) + 255) / 256 * 256 : 0;
 }
 size_t h16_bytes(const Shape& sp, const GemmPlan& p, int64_t M) {
-  return p.h16 ? h16_x_bytes(sp, p, M) + ((size_t)M * sizeof(float) + 255) / 256 * 256 : 0;
+  return p.h16 ? h16_x_bytes(sp, p, M) + (size_t)((M + 127) / 128 * 128) * sizeof(float) : 0;
 }
 
 // Act-order first gathers the columns of x into the workspace (front bytes

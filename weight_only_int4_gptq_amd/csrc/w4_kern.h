@@ -401,9 +401,12 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
   };
   constexpr int NP = Groups<GM>::kPeriods;
   constexpr int R = MT * NB * 4;
-  extern __shared__ float smem[];  // [KW][R][64] reduction buffer, then (XL) the activation rows
+  // [KW][R][64] reduction buffer; with XL the staged activation rows occupy
+  // the same bytes first (the reduction starts after a barrier), so the
+  // launch needs the larger of the two, not their sum
+  extern __shared__ float smem[];
   float* red = smem;
-  uint16_t* xlds = reinterpret_cast<uint16_t*>(smem + KW * R * 64);
+  uint16_t* xlds = reinterpret_cast<uint16_t*>(smem);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -526,6 +529,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny(const uint16_t* __restric
   }
 
   // Sum the KW waves' partial results in LDS, then bias, round and store.
+  if constexpr (XL) __syncthreads();  // every wave is done with the activation rows
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -1080,9 +1084,10 @@ __global__ void row_sums_bf16(const uint16_t* __restrict__ x, float* __restrict_
 constexpr size_t kMaxSkinnyLds = 128 * 1024;  // of the CU's 160 KiB
 
 inline size_t skinny_lds_bytes(int mt, int nb, int kw, bool xl, int64_t M, int64_t K) {
-  size_t b = (size_t)kw * mt * nb * 4 * 64 * sizeof(float);
-  if (xl) b += (size_t)(M < kXlRows ? M : kXlRows) * (size_t)(K + kXPad) * sizeof(uint16_t);
-  return b;
+  const size_t b = (size_t)kw * mt * nb * 4 * 64 * sizeof(float);
+  if (!xl) return b;
+  const size_t xb = (size_t)(M < kXlRows ? M : kXlRows) * (size_t)(K + kXPad) * sizeof(uint16_t);
+  return b > xb ? b : xb;
 }
 
 // Ring depth of a skinny configuration (from timing sweeps): double
