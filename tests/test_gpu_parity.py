@@ -572,6 +572,42 @@ def test_linear_wide_tiles_sampled(W, v):
 
 
 # ----------------------------------------------------------------------------
+# Act-order at M <= 4 on layers of more than 256 strips: the staged-activation
+# kernel on the gathered rows, every M of its range, with bias
+# ----------------------------------------------------------------------------
+
+XL_ACT_VARIANTS = [
+    # (name, group_size, has_zeros, dtype)
+    ("fp16-g128-z", 128, True, "fp16"),
+    ("bf16-g64-sym", 64, False, "bf16"),
+    ("fp16-g32-z", 32, True, "fp16"),
+]
+
+
+@pytest.mark.parametrize("v", XL_ACT_VARIANTS, ids=[v[0] for v in XL_ACT_VARIANTS])
+def test_linear_actorder_staged_gather(W, v):
+    name, gs, has_z, dtype = v
+    K, N = 1152, 4112                     # 257 strips, the last half padding
+    G = K // gs
+    rng = seeded(707, K, N, gs, int(has_z))
+    lo, hi = (0.002, 0.02) if dtype == "fp16" else (0.001, 0.01)
+    qweight = random_words(rng, (K // 8, N))
+    qzeros = random_words(rng, (G, N // 8)) if has_z else None
+    scales = uniform_scales(rng, (G, N), lo, hi, dtype)
+    g_idx = actorder_gidx(rng, K, gs)
+    Lyr = _prepare(W, "std", K, N, gs, has_z, True, dtype, qweight, qzeros, scales, g_idx)
+    bias = uniform_scales(seeded(708, N), (N,), -1.0, 1.0, dtype)
+    for M in (1, 2, 3, 4):
+        say(f"act-order staged gather {name} M={M} kernel={Lyr.kernel_name(M)}")
+        assert Lyr.kernel_name(M) == "w4_skinny_lds_k8", Lyr.kernel_name(M)
+        x = normal_acts(seeded(709, M, K), (M, K), dtype)
+        y, guard = _run_linear(W, Lyr, x, bias, guard_rows=2)
+        assert (guard.view(np.uint16) == 0x7F7F).all(), "write past row M"
+        ref = O.reference_linear(x, "std", dtype, qweight, qzeros, scales, gs, g_idx=g_idx, bias=bias)
+        _assert_close(y, ref, dtype, f"{name} M={M} (all {M * N} outputs)")
+
+
+# ----------------------------------------------------------------------------
 # bf16 at large M: the 32x32x16 kernel on an exact fp16 copy of x, each row
 # scaled by a power of two into fp16's exact range
 # ----------------------------------------------------------------------------
