@@ -51,8 +51,8 @@
 // that brings its largest finite magnitude into [2^14, 2^15), and the
 // epilogue multiplies that row's result by 2^e.  So every value of the row
 // down to 2^-29 of its largest is exact; smaller ones are rounded to fp16's
-// subnormal grid, an error below 2^-40 of the row's largest magnitude per
-// element.  Scales, bias and output stay bf16.
+// subnormal grid, an error of at most 2^-39 of the row's largest magnitude
+// per element.  Scales, bias and output stay bf16.
 //
 // Workgroup -> tile: the dispatcher hands consecutive workgroups to the
 // eight XCDs in turn; the grid is remapped so that each XCD walks a
@@ -392,12 +392,11 @@ __global__ __launch_bounds__(64 * WM * WN, OB16 && Groups<GM>::kPeriods == 1 ? 2
 
 // xh[m][k] = fp16(x[m][k] 2^-e_m) and rowf[m] = 2^e_m for bf16 x [M][K]
 // (K a multiple of 8): e_m brings the row's largest finite magnitude into
-// [2^14, 2^15) (clamped to [-126, 113]; 0 for a row without a finite nonzero
-// value).  One workgroup
-// per row: the row's maximum first, then the conversion (round to nearest
-// even, exact in fp16's normal range).  CH > 0: rows of at most 256 CH
-// 16-byte chunks, kept in registers between the two passes (one read of x);
-// CH = 0: any K, read twice.
+// [2^14, 2^15) (e_m >= -126; 0 for a row without a finite nonzero value).
+// One workgroup per row: the row's maximum first, then the conversion
+// (round to nearest even, exact in fp16's normal range).  CH > 0: rows of
+// at most 256 CH 16-byte chunks, kept in registers between the two passes
+// (one read of x); CH = 0: any K, read twice.
 template <int CH>
 __global__ __launch_bounds__(256) void bf16_rows_to_f16(const uint16_t* __restrict__ x, uint16_t* __restrict__ xh,
                                                         float* __restrict__ rowf, int64_t M, int64_t K) {
@@ -410,7 +409,7 @@ __global__ __launch_bounds__(256) void bf16_rows_to_f16(const uint16_t* __restri
     for (int j = 0; j < 4; ++j) {
       const float lo = __builtin_fabsf(bit_as<float>(w[j] << 16));
       const float hi = __builtin_fabsf(bit_as<float>(w[j] & 0xFFFF0000u));
-      // infinities and NaNs leave the row unscaled (they stay what they are)
+      // infinities and NaNs do not count (scaled, they stay what they are)
       if (lo < __builtin_inff() && lo > mx) mx = lo;
       if (hi < __builtin_inff() && hi > mx) mx = hi;
     }
